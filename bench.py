@@ -1,0 +1,298 @@
+"""Throughput of Newton-Schulz orthogonalization on one MI355X.
+
+Default workload: one Llama-8B MLP-shaped matrix, 4096 x 14336 bf16, with
+N(0,1) entries times log-uniform column scales in [1e-3, 1], orthogonalized
+by the Gram form (5 tuned steps, restart before step 3).  A step is one full
+ns_orthogonalize call on a matrix already resident in HBM: norm, staging,
+every product, and the final cast back into the caller's buffer.  The call
+works in place, so each step orthogonalizes the previous step's output; the
+products are dense, so the work does not depend on the values.
+
+Prints one JSON line.  Besides the driver's fields it carries:
+  tflops / mfma_frac     algorithmic (symmetric-aware) TFLOP/s of the whole
+                         step and its fraction of the fp16/bf16 dense peak;
+  standard_form          the same measurement for the standard form;
+  roofline               the dominant kernel's achieved rate (HIP events
+                         around its launches inside the timed region);
+  kernels                per-kernel-kind average times from the same events;
+  cpu_baseline           the fp64 oracle on the host cores (bounded sample).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("NS orthogonalizations/sec + TFLOP/s (MFMA % of peak) at "
+          "4096x14336 bf16")
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b-mlp",
+                    choices=["llama8b-mlp", "llama8b-down", "llama8b-square",
+                             "moe-experts", "moe-experts-t", "small-fp32"])
+    ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
+    ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
+    ap.add_argument("--restart-mask", type=int, default=1 << 3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-standard", action="store_true",
+                    help="skip the standard-form companion measurement")
+    return ap.parse_args()
+
+
+def workload_input(name):
+    import workloads
+    if name == "llama8b-mlp":
+        return workloads.llama8b((4096, 14336)), "bf16"
+    if name == "llama8b-down":
+        return workloads.llama8b((14336, 4096)), "bf16"
+    if name == "llama8b-square":
+        return workloads.llama8b((4096, 4096)), "bf16"
+    if name == "moe-experts":
+        return workloads.moe_experts(128, 2048, 1408), "bf16"
+    if name == "moe-experts-t":
+        return workloads.moe_experts(128, 1408, 2048), "bf16"
+    if name == "small-fp32":
+        return workloads.small_fp32(), "fp32"
+    raise ValueError(name)
+
+
+class Events:
+    """Raw hipEvent_t handles from the HIP runtime torch loaded."""
+
+    def __init__(self, count):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [
+            ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * count)()
+        for i in range(count):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = h
+        self.count = count
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i],
+                                        self.arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for i in range(self.count):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def make_trace(events, capacity, kind_mask):
+    from newton_schulz_matrix_amd._binding import Trace
+    t = Trace()
+    t.events = ctypes.cast(events.arr, ctypes.POINTER(ctypes.c_void_p))
+    kinds = (ctypes.c_int32 * capacity)()
+    flops = (ctypes.c_double * capacity)()
+    nbytes = (ctypes.c_double * capacity)()
+    t.kinds = kinds
+    t.flops = flops
+    t.bytes = nbytes
+    t.capacity = capacity
+    t.count = 0
+    t.kind_mask = kind_mask
+    t._keep = (kinds, flops, nbytes)
+    return t
+
+
+def trace_stats(events, t):
+    from newton_schulz_matrix_amd._binding import KERNEL_KINDS
+    stats = {}
+    for i in range(t.count):
+        kind = KERNEL_KINDS[t.kinds[i]]
+        ms = events.elapsed_ms(2 * i, 2 * i + 1)
+        s = stats.setdefault(kind, {"launches": 0, "ms": 0.0, "flops": 0.0,
+                                    "bytes": 0.0})
+        s["launches"] += 1
+        s["ms"] += ms
+        s["flops"] += t.flops[i]
+        s["bytes"] += t.bytes[i]
+    return stats
+
+
+def run_form(x, mode, steps, warmup, args, trace_kinds=None):
+    """Warm up, then time `steps` calls; optionally trace some kernel kinds."""
+    import torch
+    import newton_schulz_matrix_amd as nsa
+    batched = x.dim() == 3
+    call = nsa.orthogonalize_batched if batched else nsa.orthogonalize
+    rows, cols = x.shape[-2], x.shape[-1]
+    ws = torch.empty(nsa.workspace_size(rows, cols, x.shape[0] if batched
+                                        else 1, x.dtype, mode,
+                                        args.restart_mask, args.internal)
+                     + 256, dtype=torch.uint8, device=x.device)
+    kw = dict(mode=mode, restart_mask=args.restart_mask,
+              internal=args.internal, workspace=ws)
+    # Warm-up with every kind traced to find the dominant kernel.
+    per_call = 64
+    ev = Events(2 * per_call * max(warmup, 1))
+    tr = make_trace(ev, per_call * max(warmup, 1), 0xFFFFFFFF)
+    for _ in range(max(warmup, 1)):
+        call(x, trace=tr, **kw)
+    torch.cuda.synchronize()
+    warm = trace_stats(ev, tr)
+    ev.close()
+    dominant = max(warm, key=lambda k: warm[k]["ms"])
+    mask = 0
+    kinds = trace_kinds if trace_kinds is not None else [dominant]
+    from newton_schulz_matrix_amd._binding import KERNEL_KINDS
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    ev = Events(2 * per_call * steps)
+    tr = make_trace(ev, per_call * steps, mask)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        call(x, trace=tr, **kw)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    timed = trace_stats(ev, tr)
+    ev.close()
+    return {"ms_per_step": total_ms / steps, "wall_s": wall,
+            "dominant": dominant, "warm_kernels": warm, "timed_kernels": timed}
+
+
+def cpu_baseline(m_cpu, mode, restart_mask):
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    m64 = m_cpu.double().numpy()
+    restarts = tuple(k for k in range(1, 33) if (restart_mask >> k) & 1)
+    t0 = time.perf_counter()
+    if mode == "gram":
+        oracle.ns_gram(m64, 5, oracle.TUNED_ABC, restarts)
+    else:
+        oracle.ns_standard(m64, 5, oracle.TUNED_ABC)
+    dt = time.perf_counter() - t0
+    threads = [d.get("num_threads") for d in threadpool_info()
+               if d.get("user_api") == "blas"]
+    cores = int(max(threads)) if threads else len(os.sched_getaffinity(0))
+    return {"value": 1.0 / dt, "unit": "orth/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one full {m64.shape[0]}x{m64.shape[1]} {mode}-form "
+                      f"orthogonalization in fp64 (numpy/OpenBLAS), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} "
+              "is not supported (multi-GPU sharding is described in the design "
+              "notes, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import newton_schulz_matrix_amd as nsa
+    from newton_schulz_matrix_amd.flops import ns_flops
+
+    dev = torch.device("cuda:0")
+    m_cpu, io = workload_input(args.workload)
+    x = m_cpu.to(dev)
+    rows, cols = x.shape[-2], x.shape[-1]
+    batch = x.shape[0] if x.dim() == 3 else 1
+    internal = args.internal or ("fp16" if io != "fp32" else "fp32")
+    dtype = {"fp16": "f16", "bf16": "bf16", "fp32": "f32"}[internal]
+
+    res = run_form(x, args.mode, args.steps, args.warmup, args)
+    ms = res["ms_per_step"]
+    flops = batch * ns_flops(rows, cols, 5, args.mode, args.restart_mask)
+    value = batch * 1000.0 / ms
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    dom = res["dominant"]
+    ks = res["timed_kernels"].get(dom) or res["warm_kernels"][dom]
+    avg_ms = ks["ms"] / ks["launches"]
+    if dom in ("norm", "stage", "threshold"):
+        achieved = ks["bytes"] / ks["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        achieved = ks["flops"] / ks["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved,
+                "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = avg_ms
+    roof["launches_timed"] = ks["launches"]
+
+    kernels = {}
+    for k, s in res["warm_kernels"].items():
+        avg = s["ms"] / s["launches"]
+        entry = {"launches_per_step": s["launches"] / max(args.warmup, 1),
+                 "avg_ms": avg}
+        if s["flops"] > 0:
+            entry["tflops"] = s["flops"] / s["launches"] / (avg * 1e-3) / 1e12
+        else:
+            entry["gbs"] = s["bytes"] / s["launches"] / (avg * 1e-3) / 1e9
+        kernels[k] = entry
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "orth/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": rows, "cols": cols,
+                   "batch": batch, "io_dtype": io, "mode": args.mode,
+                   "ns_steps": 5, "abc": list(nsa.TUNED_ABC),
+                   "restart_mask": args.restart_mask,
+                   "parallelism": "single-gpu"},
+        "tflops": tflops,
+        "mfma_frac": tflops / PEAK_TFLOPS[dtype],
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_standard and args.mode == "gram":
+        std = run_form(x, "standard", max(args.steps // 2, 3), 2, args)
+        sflops = batch * ns_flops(rows, cols, 5, "standard")
+        out["standard_form"] = {
+            "ms_per_step": std["ms_per_step"],
+            "orth_per_s": batch * 1000.0 / std["ms_per_step"],
+            "tflops": sflops / (std["ms_per_step"] * 1e-3) / 1e12,
+            "gram_speedup": std["ms_per_step"] / ms}
+    if not args.no_cpu_baseline:
+        sample = m_cpu if m_cpu.dim() == 2 else m_cpu[0]
+        cb = cpu_baseline(sample, args.mode, args.restart_mask)
+        if m_cpu.dim() == 3:
+            cb["sample"] += " (one expert of the batch)"
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,18 @@
+"""Newton-Schulz orthogonalization for AMD Instinct MI355X (gfx950).
+
+Python face of ``libnsortho.so``: the standard and Gram forms of quintic
+Newton-Schulz (Muon's approximate polar factor), a batched launcher for
+equal-shape expert matrices and the ROOT soft-threshold split.  The HIP
+library does all the work; this package only marshals arguments.
+"""
+
+from .flops import gram_flops, ns_flops, standard_flops
+from ._binding import (NS_MAX_STEPS, TUNED_ABC, NSError, lib, orthogonalize,
+                       orthogonalize_batched, soft_threshold_split,
+                       status_string, workspace_size)
+
+__all__ = [
+    "NS_MAX_STEPS", "TUNED_ABC", "NSError", "lib", "orthogonalize",
+    "orthogonalize_batched", "soft_threshold_split", "status_string",
+    "workspace_size", "gram_flops", "ns_flops", "standard_flops",
+]

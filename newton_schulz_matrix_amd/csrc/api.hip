@@ -1,0 +1,529 @@
+// api.hip - host side of libnsortho: argument checks, workspace layout and
+// the launch sequence of both Newton-Schulz forms on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/nsortho.h"
+#include "products.hpp"
+#include "stage.hpp"
+#include "threshold.hpp"
+
+using namespace nsk;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kPrescaleExp16 = 10;  // X is held as 2^10 * X in 16-bit storage
+constexpr int kMaxPartials = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int elem_size(ns_dtype d) { return d == NS_FP32 ? 4 : 2; }
+
+// Shapes and workspace layout of one call.
+struct Plan {
+  int64_t rows = 0, cols = 0, n = 0, m = 0, n_pad = 0, m_pad = 0;
+  int64_t batch = 1;
+  bool transposed = false;
+  int tile = 256;
+  ns_dtype io = NS_BF16, internal = NS_FP16;
+  ns_mode mode = NS_STANDARD;
+  int esz = 2;
+  int partials = 1;
+  int nn_count = 2;
+  int64_t x_elems = 0, nn_elems = 0;
+  size_t off_partial = 0, off_x[2] = {0, 0}, off_nn[4] = {0, 0, 0, 0}, total = 0;
+};
+
+bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
+  const int req = opt ? opt->internal : -1;
+  if (io == NS_FP32) {
+    if (req != -1 && req != NS_FP32) return false;
+    *out = NS_FP32;
+    return true;
+  }
+  if (io != NS_BF16 && io != NS_FP16) return false;
+  if (req == -1 || req == NS_FP16) {
+    *out = NS_FP16;
+    return true;
+  }
+  if (req == NS_BF16) {
+    *out = NS_BF16;
+    return true;
+  }
+  return false;
+}
+
+// Tile edge: 256 when the small side is large and needs no extra padding
+// for it, else 128.
+int pick_tile(int64_t n) {
+  if (n >= 512 && round_up(n, 256) == round_up(n, 128)) return 256;
+  return 128;
+}
+
+ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_mode mode, const ns_options* opt,
+                    Plan* p) {
+  if (rows < 1 || cols < 1 || batch < 1 || batch > 65535) return NS_ERR_INVALID_ARG;
+  if (mode != NS_STANDARD && mode != NS_GRAM) return NS_ERR_INVALID_ARG;
+  if (io != NS_BF16 && io != NS_FP16 && io != NS_FP32) return NS_ERR_UNSUPPORTED_DTYPE;
+  ns_dtype internal;
+  if (!resolve_internal(io, opt, &internal)) return NS_ERR_UNSUPPORTED_DTYPE;
+  p->rows = rows;
+  p->cols = cols;
+  p->batch = batch;
+  p->io = io;
+  p->internal = internal;
+  p->mode = mode;
+  p->transposed = rows > cols;
+  p->n = p->transposed ? cols : rows;
+  p->m = p->transposed ? rows : cols;
+  p->tile = pick_tile(p->n);
+  p->n_pad = round_up(p->n, p->tile);
+  p->m_pad = round_up(p->m, p->tile);
+  p->esz = elem_size(internal);
+  p->x_elems = p->n_pad * p->m_pad;
+  p->nn_elems = p->n_pad * p->n_pad;
+  // Offsets inside one matrix are 32-bit in the kernels' index math.
+  if ((double)p->x_elems * p->esz >= 2147483648.0 || p->n_pad > 65536) return NS_ERR_INVALID_ARG;
+  const int64_t want = (p->n + 15) / 16;
+  p->partials = (int)(want < 1 ? 1 : (want > kMaxPartials ? kMaxPartials : want));
+  p->nn_count = mode == NS_GRAM ? 4 : 2;
+  size_t off = 0;
+  p->off_partial = off;
+  off = align_up(off + (size_t)batch * p->partials * sizeof(double));
+  for (int i = 0; i < 2; ++i) {
+    p->off_x[i] = off;
+    off = align_up(off + (size_t)batch * p->x_elems * p->esz);
+  }
+  for (int i = 0; i < p->nn_count; ++i) {
+    p->off_nn[i] = off;
+    off = align_up(off + (size_t)batch * p->nn_elems * p->esz);
+  }
+  p->total = off;
+  return NS_OK;
+}
+
+ns_status hip_status(hipError_t e) { return e == hipSuccess ? NS_OK : NS_ERR_HIP; }
+
+// Brackets launches with the caller's events when a trace is attached.
+struct Tracer {
+  ns_trace* t;
+  hipStream_t st;
+  template <class F>
+  hipError_t run(ns_kernel_kind kind, double flops, double bytes, F&& launch) const {
+    const bool rec = t && t->events && ((t->kind_mask >> (int)kind) & 1u) && t->count >= 0 &&
+                     t->count < t->capacity;
+    const int i = rec ? t->count : -1;
+    hipError_t e;
+    if (rec && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(t->events[2 * i]), st)) != hipSuccess) return e;
+    if ((e = launch()) != hipSuccess) return e;
+    if (rec) {
+      if ((e = hipEventRecord(reinterpret_cast<hipEvent_t>(t->events[2 * i + 1]), st)) != hipSuccess) return e;
+      if (t->kinds) t->kinds[i] = (int32_t)kind;
+      if (t->flops) t->flops[i] = flops;
+      if (t->bytes) t->bytes[i] = bytes;
+      t->count = i + 1;
+    }
+    return hipSuccess;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Kernel launchers.
+// ---------------------------------------------------------------------------
+template <typename T, int TILE, bool GRAM_INPUT>
+hipError_t launch_sym(const SymArgs<T>& a, int64_t batch, hipStream_t s) {
+  const size_t smem = 4 * (size_t)TILE * kRowBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym<T, TILE, GRAM_INPUT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (attr != hipSuccess) return attr;
+  const int ntri = a.tiles * (a.tiles + 1) / 2;
+  hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT>), dim3(ntri, (unsigned)batch), dim3(kThreads), smem, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, typename OutT, int TILE>
+hipError_t launch_nn(const NNArgs<T, OutT>& a, int64_t batch, hipStream_t s) {
+  const size_t smem = 4 * (size_t)TILE * kRowBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_nn<T, OutT, TILE>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((k_nn<T, OutT, TILE>), dim3(a.tiles_m * a.tiles_n, (unsigned)batch), dim3(kThreads), smem, s, a);
+  return hipGetLastError();
+}
+
+// One Newton-Schulz run over a batch, for internal type T and I/O type IO.
+template <typename T, typename IO>
+struct Runner {
+  const Plan& p;
+  char* ws;
+  hipStream_t st;
+  IO* user;
+  int64_t ld, bstride;
+  const ns_options* opt;
+  Tracer tr;
+
+  T* xbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_x[i]); }
+  T* nnbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_nn[i]); }
+
+  // C = beta*E + gamma * L R^T on upper tiles, mirrored.  L and R are the
+  // X buffers (K = m_pad) or n x n buffers (K = n_pad).
+  template <int TILE>
+  hipError_t sym(const T* L, const T* R, int K, int ldk, const T* E, float beta, float gamma, T* C, T* C2,
+                 float delta) const {
+    SymArgs<T> a;
+    a.L = L;
+    a.R = R;
+    a.E = E;
+    a.C = C;
+    a.C2 = C2;
+    // X X^T reads an X buffer (stride n_pad * m_pad); the others read n x n
+    // buffers.
+    const bool gram = (L == xbuf(0) || L == xbuf(1));
+    const int64_t xs = gram ? p.x_elems : p.nn_elems;
+    a.sL = xs;
+    a.sR = xs;
+    a.sE = p.nn_elems;
+    a.sC = p.nn_elems;
+    a.sC2 = p.nn_elems;
+    a.ldk = ldk;
+    a.ldn = (int)p.n_pad;
+    a.K = K;
+    a.tiles = (int)(p.n_pad / TILE);
+    a.n_real = (int)p.n;
+    a.alpha_unused = 0.f;
+    a.beta = beta;
+    a.gamma = gamma;
+    a.delta = delta;
+    const double n = (double)p.n, bt = (double)p.batch, es = sizeof(T);
+    const double inner = gram ? (double)p.m : n;
+    const double flops = n * n * inner * bt;
+    double bytes = (L == R ? 1.0 : 2.0) * n * inner * es + n * n * es * (1.0 + (E ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
+    bytes *= bt;
+    if (gram)
+      return tr.run(NS_KERNEL_GRAM, flops, bytes, [&] { return launch_sym<T, TILE, true>(a, p.batch, st); });
+    return tr.run(NS_KERNEL_SYM, flops, bytes, [&] { return launch_sym<T, TILE, false>(a, p.batch, st); });
+  }
+
+  template <int TILE>
+  hipError_t nn_internal(const T* B, const T* X, const T* E, float alpha, T* Y) const {
+    NNArgs<T, T> a;
+    a.B = B;
+    a.X = X;
+    a.E = E;
+    a.Y = Y;
+    a.sB = p.nn_elems;
+    a.sX = p.x_elems;
+    a.sE = p.x_elems;
+    a.sY = p.x_elems;
+    a.ldb = (int)p.n_pad;
+    a.ldx = (int)p.m_pad;
+    a.ldy = p.m_pad;
+    a.K = (int)p.n_pad;
+    a.tiles_m = (int)(p.n_pad / TILE);
+    a.tiles_n = (int)(p.m_pad / TILE);
+    a.n_real = (int)p.n;
+    a.m_real = (int)p.m;
+    a.transpose_out = 0;
+    a.final_out = 0;
+    a.alpha = alpha;
+    a.gamma = 1.f;
+    a.out_scale = 1.f;
+    a.d_status = nullptr;
+    const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
+    const double bytes = bt * (n * n * es + n * m * es * (2.0 + (E ? 1.0 : 0.0)));
+    return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
+                  [&] { return launch_nn<T, T, TILE>(a, p.batch, st); });
+  }
+
+  template <int TILE>
+  hipError_t nn_final(const T* B, const T* X, const T* E, float alpha, float out_scale) const {
+    NNArgs<T, IO> a;
+    a.B = B;
+    a.X = X;
+    a.E = E;
+    a.Y = user;
+    a.sB = p.nn_elems;
+    a.sX = p.x_elems;
+    a.sE = p.x_elems;
+    a.sY = bstride;
+    a.ldb = (int)p.n_pad;
+    a.ldx = (int)p.m_pad;
+    a.ldy = ld;
+    a.K = (int)p.n_pad;
+    a.tiles_m = (int)(p.n_pad / TILE);
+    a.tiles_n = (int)(p.m_pad / TILE);
+    a.n_real = (int)p.n;
+    a.m_real = (int)p.m;
+    a.transpose_out = p.transposed ? 1 : 0;
+    a.final_out = 1;
+    a.alpha = alpha;
+    a.gamma = 1.f;
+    a.out_scale = out_scale;
+    a.d_status = opt ? opt->d_status : nullptr;
+    const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
+    const double bytes = bt * (n * n * es + n * m * es * (1.0 + (E ? 1.0 : 0.0)) + n * m * sizeof(IO));
+    return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
+                  [&] { return launch_nn<T, IO, TILE>(a, p.batch, st); });
+  }
+
+  hipError_t stage(float prescale, float eps) const {
+    double* partial = reinterpret_cast<double*>(ws + p.off_partial);
+    const bool vec_ok = (p.cols % (16 / sizeof(IO)) == 0) && (ld % (16 / sizeof(IO)) == 0) &&
+                        ((reinterpret_cast<uintptr_t>(user) & 15) == 0) &&
+                        (p.batch == 1 || bstride % (16 / sizeof(IO)) == 0);
+    const double elems = (double)p.rows * (double)p.cols * (double)p.batch;
+    hipError_t e = tr.run(NS_KERNEL_NORM, 0.0, elems * sizeof(IO), [&] {
+      hipLaunchKernelGGL((k_sumsq<IO>), dim3(p.partials, (unsigned)p.batch), dim3(kStageThreads), 0, st, user,
+                         p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, partial, p.partials);
+      return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
+    return tr.run(NS_KERNEL_STAGE, 0.0, elems * (sizeof(IO) + sizeof(T)), [&] {
+      if (!p.transposed) {
+        hipLaunchKernelGGL((k_stage_rows<IO, T>), dim3((unsigned)p.n_pad, (unsigned)p.batch), dim3(kStageThreads),
+                           0, st, user, p.rows, p.cols, ld, bstride, partial, p.partials, prescale, eps, xbuf(0),
+                           p.m_pad, p.x_elems);
+      } else {
+        const int tj = (int)(p.m_pad / 64);
+        const int ti = (int)(p.n_pad / 64);
+        hipLaunchKernelGGL((k_stage_transpose<IO, T>), dim3((unsigned)(ti * tj), (unsigned)p.batch),
+                           dim3(kStageThreads), 0, st, user, p.rows, p.cols, ld, bstride, partial, p.partials,
+                           prescale, eps, xbuf(0), p.m_pad, p.x_elems, tj);
+      }
+      return hipGetLastError();
+    });
+  }
+
+  template <int TILE>
+  hipError_t run(int steps, const float* a, const float* b, const float* c, float eps) const {
+    const int pe = (sizeof(T) == 2) ? kPrescaleExp16 : 0;
+    const float prescale = ldexpf(1.f, pe);
+    const float unscale = ldexpf(1.f, -pe);
+    const float gram_scale = ldexpf(1.f, -2 * pe);
+    const int mp = (int)p.m_pad, np = (int)p.n_pad;
+    hipError_t e = stage(prescale, eps);
+    if (e != hipSuccess) return e;
+    int xi = 0;
+    if (p.mode == NS_STANDARD) {
+      T* A = nnbuf(0);
+      T* B = nnbuf(1);
+      for (int k = 0; k < steps; ++k) {
+        T* X = xbuf(xi);
+        if ((e = sym<TILE>(X, X, mp, mp, nullptr, 0.f, gram_scale, A, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(A, A, np, np, A, b[k], c[k], B, nullptr, 0.f)) != hipSuccess) return e;
+        if (k + 1 < steps) {
+          if ((e = nn_internal<TILE>(B, X, X, a[k], xbuf(xi ^ 1))) != hipSuccess) return e;
+          xi ^= 1;
+        } else {
+          if ((e = nn_final<TILE>(B, X, X, a[k], unscale)) != hipSuccess) return e;
+        }
+      }
+      return hipSuccess;
+    }
+    // Gram form.
+    const uint32_t mask = opt ? opt->restart_mask : (1u << 3);
+    T* R = nnbuf(0);
+    T* Z = nnbuf(1);
+    T* Qb[2] = {nnbuf(2), nnbuf(3)};
+    int qi = 0;
+    if ((e = sym<TILE>(xbuf(0), xbuf(0), mp, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f)) != hipSuccess) return e;
+    bool fresh = true;
+    for (int k = 1; k <= steps; ++k) {
+      if (k > 1 && ((mask >> k) & 1u)) {
+        if ((e = nn_internal<TILE>(Qb[qi], xbuf(xi), nullptr, 0.f, xbuf(xi ^ 1))) != hipSuccess) return e;
+        xi ^= 1;
+        if ((e = sym<TILE>(xbuf(xi), xbuf(xi), mp, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f)) != hipSuccess)
+          return e;
+        fresh = true;
+      }
+      const float ak = a[k - 1], bk = b[k - 1], ck = c[k - 1];
+      // Z' = b R + c R^2; at a fresh start Q = a I + Z' comes out of the same
+      // epilogue.
+      if ((e = sym<TILE>(R, R, np, np, R, bk, ck, Z, fresh ? Qb[qi] : nullptr, ak)) != hipSuccess) return e;
+      if (!fresh) {
+        if ((e = sym<TILE>(Z, Qb[qi], np, np, Qb[qi], ak, 1.f, Qb[qi ^ 1], nullptr, 0.f)) != hipSuccess) return e;
+        qi ^= 1;
+      }
+      fresh = false;
+      const bool need_r = k < steps && !((mask >> (k + 1)) & 1u);
+      if (need_r) {
+        T* V = Qb[qi ^ 1];
+        if ((e = sym<TILE>(Z, R, np, np, R, ak, 1.f, V, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(Z, V, np, np, V, ak, 1.f, R, nullptr, 0.f)) != hipSuccess) return e;
+      }
+    }
+    return nn_final<TILE>(Qb[qi], xbuf(xi), nullptr, 0.f, unscale);
+  }
+};
+
+template <typename T, typename IO>
+ns_status run_typed(const Plan& p, void* X, int64_t ld, int64_t bstride, int steps, const float* a, const float* b,
+                    const float* c, const ns_options* opt, void* ws, hipStream_t st) {
+  Runner<T, IO> r{p, reinterpret_cast<char*>(ws), st, reinterpret_cast<IO*>(X), ld, bstride, opt,
+                  Tracer{opt ? opt->trace : nullptr, st}};
+  const float eps = opt ? opt->eps : 1e-7f;
+  hipError_t e = (p.tile == 256) ? r.template run<256>(steps, a, b, c, eps) : r.template run<128>(steps, a, b, c, eps);
+  return hip_status(e);
+}
+
+ns_status check_coefficients(int32_t steps, const float* a, const float* b, const float* c, ns_mode mode,
+                             uint32_t mask, ns_dtype internal) {
+  if (steps < 1 || steps > NS_MAX_STEPS || !a || !b || !c) return NS_ERR_INVALID_ARG;
+  for (int k = 0; k < steps; ++k)
+    if (!isfinite(a[k]) || !isfinite(b[k]) || !isfinite(c[k])) return NS_ERR_INVALID_ARG;
+  if (mode == NS_GRAM && internal != NS_FP32) {
+    // The accumulated Q is a product of factors a_k I + ... whose largest
+    // eigenvalue can reach |a_k| per step; keep it inside fp16 range.
+    double run = 1.0;
+    for (int k = 1; k <= steps; ++k) {
+      if (k > 1 && ((mask >> k) & 1u)) run = 1.0;
+      run *= fabs((double)a[k - 1]);
+      if (run >= 32768.0) return NS_ERR_INVALID_ARG;
+    }
+  }
+  return NS_OK;
+}
+
+ns_status orthogonalize_impl(void* X, int64_t batch, int64_t rows, int64_t cols, int64_t ld, int64_t bstride,
+                             ns_dtype dtype, int32_t steps, const float* a, const float* b, const float* c,
+                             ns_mode mode, const ns_options* opt, void* ws, size_t ws_bytes, ns_stream_t stream) {
+  if (!X) return NS_ERR_INVALID_ARG;
+  if (ld < cols) return NS_ERR_INVALID_ARG;
+  if (batch > 1 && bstride < rows * ld) return NS_ERR_INVALID_ARG;
+  Plan p;
+  ns_status s = make_plan(rows, cols, batch, dtype, mode, opt, &p);
+  if (s != NS_OK) return s;
+  if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
+  const uint32_t mask = opt ? opt->restart_mask : (1u << 3);
+  if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal)) != NS_OK) return s;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == NS_FP32) return run_typed<float, float>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
+  if (dtype == NS_BF16) {
+    if (p.internal == NS_FP16) return run_typed<_Float16, __bf16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
+    return run_typed<__bf16, __bf16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
+  }
+  if (p.internal == NS_FP16) return run_typed<_Float16, _Float16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
+  return run_typed<__bf16, _Float16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
+}
+
+// Soft-threshold workspace: select state + three histograms.
+size_t threshold_ws_bytes() { return align_up(sizeof(SelectState)) + align_up(3 * kHistBins * sizeof(uint32_t)); }
+
+template <typename IO>
+ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float lambda, float mult,
+                          float* d_lambda_out, void* ws, hipStream_t st) {
+  char* w = reinterpret_cast<char*>(ws);
+  SelectState* state = reinterpret_cast<SelectState*>(w);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(w + align_up(sizeof(SelectState)));
+  const IO* m = reinterpret_cast<const IO*>(M);
+  const int64_t blocks64 = (numel + 255) / 256;
+  const unsigned grid = (unsigned)(blocks64 < 2048 ? blocks64 : 2048);
+  const uint64_t rank = (uint64_t)((numel + 1) / 2);
+  hipLaunchKernelGGL(k_select_init, dim3((3 * kHistBins + 255) / 256), dim3(256), 0, st, state, hist, 3 * kHistBins,
+                     rank);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return NS_ERR_HIP;
+  if (lambda >= 0.f) {
+    hipLaunchKernelGGL(k_set_lambda, dim3(1), dim3(64), 0, st, state, lambda, d_lambda_out);
+  } else {
+    constexpr int kb = KeyOf<IO>::kBits;
+    // Digits from the top, at most 11 bits each.
+    int shifts[3], bits[3], npass = 0;
+    int hi = kb;
+    while (hi > 0) {
+      const int nbits = hi >= 11 ? 11 : hi;
+      shifts[npass] = hi - nbits;
+      bits[npass] = nbits;
+      hi -= nbits;
+      ++npass;
+    }
+    for (int ps = 0; ps < npass; ++ps) {
+      uint32_t* h = hist + ps * kHistBins;
+      hipLaunchKernelGGL((k_radix_hist<IO>), dim3(grid), dim3(kHistThreads), 0, st, m, numel, state, shifts[ps],
+                         bits[ps], h);
+      hipLaunchKernelGGL((k_radix_pick<IO>), dim3(1), dim3(kHistThreads), 0, st, state, h, shifts[ps], bits[ps],
+                         ps == npass - 1 ? 1 : 0, mult, -1.f, d_lambda_out);
+    }
+  }
+  hipLaunchKernelGGL((k_clip_split<IO>), dim3(grid), dim3(256), 0, st, m, reinterpret_cast<IO*>(B),
+                     reinterpret_cast<IO*>(O), numel, state);
+  return hip_status(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" {
+
+void ns_options_default(ns_options* opt) {
+  if (!opt) return;
+  opt->restart_mask = 1u << 3;
+  opt->eps = 1e-7f;
+  opt->internal = -1;
+  opt->d_status = nullptr;
+  opt->trace = nullptr;
+}
+
+size_t ns_workspace_size(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode,
+                         const ns_options* opt) {
+  Plan p;
+  if (make_plan(rows, cols, batch, dtype, mode, opt, &p) != NS_OK) return 0;
+  return p.total;
+}
+
+ns_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, ns_dtype dtype, int32_t steps,
+                           const float* a, const float* b, const float* c, ns_mode mode, const ns_options* opt,
+                           void* workspace, size_t workspace_bytes, ns_stream_t stream) {
+  return orthogonalize_impl(X, 1, rows, cols, ld, rows * ld, dtype, steps, a, b, c, mode, opt, workspace,
+                            workspace_bytes, stream);
+}
+
+ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                                   int64_t batch_stride, ns_dtype dtype, int32_t steps, const float* a,
+                                   const float* b, const float* c, ns_mode mode, const ns_options* opt,
+                                   void* workspace, size_t workspace_bytes, ns_stream_t stream) {
+  return orthogonalize_impl(X, batch, rows, cols, ld, batch_stride, dtype, steps, a, b, c, mode, opt, workspace,
+                            workspace_bytes, stream);
+}
+
+size_t ns_soft_threshold_workspace_size(int64_t numel, ns_dtype dtype) {
+  if (numel < 1) return 0;
+  if (dtype != NS_BF16 && dtype != NS_FP16 && dtype != NS_FP32) return 0;
+  return threshold_ws_bytes();
+}
+
+ns_status ns_soft_threshold_split(const void* M, void* B, void* O, int64_t numel, ns_dtype dtype, float lambda,
+                                  float mult, float* d_lambda_out, void* workspace, size_t workspace_bytes,
+                                  ns_stream_t stream) {
+  if (!M || !B || numel < 1) return NS_ERR_INVALID_ARG;
+  if (isnan(lambda) || (lambda < 0.f && !(isfinite(mult) && mult >= 0.f))) return NS_ERR_INVALID_ARG;
+  if (dtype != NS_BF16 && dtype != NS_FP16 && dtype != NS_FP32) return NS_ERR_UNSUPPORTED_DTYPE;
+  if (!workspace || workspace_bytes < threshold_ws_bytes() || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return NS_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == NS_BF16) return threshold_typed<__bf16>(M, B, O, numel, lambda, mult, d_lambda_out, workspace, st);
+  if (dtype == NS_FP16) return threshold_typed<_Float16>(M, B, O, numel, lambda, mult, d_lambda_out, workspace, st);
+  return threshold_typed<float>(M, B, O, numel, lambda, mult, d_lambda_out, workspace, st);
+}
+
+const char* ns_status_string(ns_status s) {
+  switch (s) {
+    case NS_OK: return "ok";
+    case NS_ERR_INVALID_ARG: return "invalid argument";
+    case NS_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case NS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case NS_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t ns_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+"""The C ABI: the library loads, exports every declared symbol, and its
+host-side logic (workspace sizes, argument checks) behaves as documented.
+
+Nothing here launches device work: every call either touches no device or
+fails its argument checks before anything is enqueued.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import newton_schulz_matrix_amd as nsa
+from newton_schulz_matrix_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsortho.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libnsortho.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(ns_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_api():
+    names = _declared_functions()
+    for want in ["ns_orthogonalize", "ns_orthogonalize_batched",
+                 "ns_soft_threshold_split", "ns_workspace_size",
+                 "ns_soft_threshold_workspace_size", "ns_status_string",
+                 "ns_options_default", "ns_version"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.ns_version() >= 100
+
+
+def test_status_strings():
+    for code in range(5):
+        assert B.status_string(code)
+    assert B.status_string(99) == "unknown status"
+
+
+def test_options_defaults():
+    opt = B.Options()
+    B.lib().ns_options_default(ctypes.byref(opt))
+    assert opt.restart_mask == 1 << 3
+    assert abs(opt.eps - 1e-7) < 1e-12
+    assert opt.internal == -1 and not opt.d_status
+
+
+def test_workspace_size_layout():
+    # Standard: partial sums + 2 X buffers + 2 n x n buffers (fp16 internal).
+    ws = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "standard")
+    x = 4096 * 14336 * 2
+    nn = 4096 * 4096 * 2
+    assert 2 * x + 2 * nn <= ws <= 2 * x + 2 * nn + 4096
+    wg = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "gram")
+    assert wg - ws == pytest.approx(2 * nn, abs=1024)
+    # Tall input has the same workspace as its transpose.
+    assert nsa.workspace_size(14336, 4096) == ws
+    # Ragged sizes are padded to the tile edge (128 below 512 rows).
+    w = nsa.workspace_size(200, 300, 1, torch.float16, "standard")
+    assert w >= 2 * 256 * 384 * 2 + 2 * 256 * 256 * 2
+    # fp32 doubles the buffers.
+    assert nsa.workspace_size(256, 1024, 1, torch.float32) > \
+        nsa.workspace_size(256, 1024, 1, torch.bfloat16)
+    # Batches scale linearly.
+    one = nsa.workspace_size(2048, 1408, 1, torch.bfloat16, "gram")
+    many = nsa.workspace_size(2048, 1408, 128, torch.bfloat16, "gram")
+    assert 127 * one < many <= 128 * one
+
+
+def test_workspace_size_rejects_bad_arguments():
+    lib = B.lib()
+    bad = [(0, 5, 1, 0, 0), (5, 0, 1, 0, 0), (5, 5, 0, 0, 0), (5, 5, 1, 7, 0),
+           (5, 5, 1, 0, 3), (5, 5, 70000, 0, 0)]
+    for rows, cols, batch, dt, mode in bad:
+        assert lib.ns_workspace_size(rows, cols, batch, dt, mode, None) == 0
+    # fp32 input cannot use 16-bit products; bf16 input cannot use fp32.
+    opt = B.make_options(internal="fp16")
+    assert lib.ns_workspace_size(8, 8, 1, B.NS_FP32, 0, ctypes.byref(opt)) == 0
+    opt = B.make_options(internal="fp32")
+    assert lib.ns_workspace_size(8, 8, 1, B.NS_BF16, 0, ctypes.byref(opt)) == 0
+
+
+def _call(ptr=1, rows=8, cols=8, ld=8, dtype=B.NS_BF16, steps=5, abc=None,
+          mode=B.NS_STANDARD, opt=None, ws=256, ws_bytes=1 << 40):
+    a, b, c = B._coefficients(abc or B.TUNED_ABC, max(steps, 1))
+    return B.lib().ns_orthogonalize(
+        ctypes.c_void_p(ptr), rows, cols, ld, dtype, steps, a, b, c, mode,
+        ctypes.byref(opt) if opt is not None else None, ctypes.c_void_p(ws),
+        ws_bytes, None)
+
+
+def test_orthogonalize_argument_checks():
+    inv, dt, wsp = 1, 2, 3
+    assert _call(ptr=0) == inv
+    assert _call(rows=0) == inv
+    assert _call(ld=7) == inv
+    assert _call(steps=0) == inv
+    assert _call(steps=17) == inv
+    assert _call(dtype=9) == dt
+    assert _call(mode=5) == inv
+    assert _call(ws=0) == wsp
+    assert _call(ws=128 + 256) == wsp                    # misaligned
+    assert _call(ws_bytes=16) == wsp
+    assert _call(abc=(float("nan"), 1.0, 1.0)) == inv
+    opt = B.make_options(eps=-1.0)
+    assert _call(opt=opt) == inv
+    # Gram with fp16 state: a^k must stay below 2^15 between restarts.
+    opt = B.make_options(restart_mask=0)
+    assert _call(steps=9, mode=B.NS_GRAM, opt=opt) == inv
+    opt = B.make_options(restart_mask=(1 << 4) | (1 << 7))
+    # 3 + 3 + 3 steps between restarts: 3.4445^3 < 2^15, but the check runs
+    # before the workspace check, which is what fails here.
+    assert _call(steps=9, mode=B.NS_GRAM, opt=opt, ws_bytes=16) == wsp
+
+
+def test_batched_argument_checks():
+    a, b, c = B._coefficients(B.TUNED_ABC, 5)
+    lib = B.lib()
+    # batch stride smaller than one matrix.
+    st = lib.ns_orthogonalize_batched(ctypes.c_void_p(256), 4, 8, 8, 8, 32,
+                                      B.NS_BF16, 5, a, b, c, B.NS_GRAM, None,
+                                      ctypes.c_void_p(256), 1 << 40, None)
+    assert st == 1
+
+
+def test_soft_threshold_argument_checks():
+    lib = B.lib()
+    assert lib.ns_soft_threshold_workspace_size(0, 0) == 0
+    assert lib.ns_soft_threshold_workspace_size(10, 5) == 0
+    need = lib.ns_soft_threshold_workspace_size(10, 0)
+    assert need > 0
+    args = dict(M=256, Bp=256, O=None, numel=10, dt=0, lam=-1.0, mult=3.0,
+                ws=256, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.ns_soft_threshold_split(
+            ctypes.c_void_p(a["M"]), ctypes.c_void_p(a["Bp"]),
+            ctypes.c_void_p(a["O"]), a["numel"], a["dt"], a["lam"], a["mult"],
+            None, ctypes.c_void_p(a["ws"]), a["wsb"], None)
+    assert call(M=0) == 1
+    assert call(numel=0) == 1
+    assert call(lam=float("nan")) == 1
+    assert call(mult=float("inf")) == 1
+    assert call(dt=4) == 2
+    assert call(wsb=need - 1) == 3
+    assert call(ws=0) == 3

@@ -1,0 +1,240 @@
+"""Parity of the HIP path with the fp64 oracle, element by element.
+
+Every case runs the library through its C ABI (via the ctypes binding) on
+seeded inputs and compares with the oracle on the same rounded values.  The
+bar is the relative Frobenius error ||gpu - oracle||_F / ||oracle||_F:
+1e-2 for 16-bit input and 1e-4 for fp32 input (the oracle is fp64; the
+device products accumulate in fp32 and store 16-bit or fp32 intermediates).
+Integer work (the median select and the clip decisions) is compared exactly.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import newton_schulz_matrix_amd as nsa
+
+pytestmark = pytest.mark.gpu
+
+TUNED = oracle.TUNED_ABC
+TOL = {torch.bfloat16: 1e-2, torch.float16: 1e-2, torch.float32: 1e-4}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _rel(x, ref):
+    d = np.linalg.norm(x - ref)
+    n = np.linalg.norm(ref)
+    return float(d / n) if n > 0 else float(d)
+
+
+def _restarts(mask):
+    return tuple(k for k in range(1, 33) if (mask >> k) & 1)
+
+
+def _oracle(m64, mode, steps=5, abc=TUNED, mask=1 << 3, eps=1e-7):
+    if mode == "standard":
+        return oracle.ns_standard(m64, steps, abc, eps)
+    return oracle.ns_gram(m64, steps, abc, _restarts(mask), eps)
+
+
+def _run(m_cpu, mode, steps=5, abc=TUNED, mask=1 << 3, internal=None,
+         ld_pad=0):
+    dev = _dev()
+    rows, cols = m_cpu.shape
+    if ld_pad:
+        big = torch.zeros(rows, cols + ld_pad, dtype=m_cpu.dtype)
+        big[:, :cols] = m_cpu
+        x = big.to(dev)[:, :cols]
+    else:
+        x = m_cpu.to(dev)
+    nsa.orthogonalize(x, steps=steps, abc=abc, mode=mode, restart_mask=mask,
+                      internal=internal)
+    torch.cuda.synchronize()
+    return x.double().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Small and ragged shapes, both forms, every dtype.
+# ---------------------------------------------------------------------------
+
+SHAPES = [(256, 1024), (200, 300), (300, 200), (128, 128), (1, 17), (17, 1),
+          (130, 700), (640, 512)]
+
+
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16,
+                                   torch.float32])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_parity_small(shape, dtype, mode):
+    name = {torch.bfloat16: "bf16", torch.float16: "fp16",
+            torch.float32: "fp32"}[dtype]
+    m = workloads.gaussian(shape, seed=sum(shape), dtype=name)
+    ref = _oracle(m.double().numpy(), mode)
+    out = _run(m, mode)
+    err = _rel(out, ref)
+    print(f"{shape} {name} {mode}: rel err {err:.3e}")
+    assert err < TOL[dtype]
+
+
+def test_parity_config1_fp32_both_forms():
+    m = workloads.small_fp32()
+    m64 = m.double().numpy()
+    for mode in ("standard", "gram"):
+        err = _rel(_run(m, mode), _oracle(m64, mode))
+        print(f"256x1024 fp32 {mode}: {err:.3e}")
+        assert err < 1e-4
+
+
+@pytest.mark.parametrize("internal", ["fp16", "bf16"])
+@pytest.mark.parametrize("mask", [0, 1 << 3, (1 << 2) | (1 << 4)])
+def test_parity_gram_restart_schedules(mask, internal):
+    m = workloads.column_scaled(384, 1000, seed=21, dtype="bf16")
+    ref = _oracle(m.double().numpy(), "gram", mask=mask)
+    out = _run(m, "gram", mask=mask, internal=internal)
+    err = _rel(out, ref)
+    print(f"mask {mask:#x} internal {internal}: {err:.3e}")
+    assert err < 1e-2
+
+
+def test_parity_bf16_internal_standard():
+    m = workloads.gaussian((256, 1024), seed=22, dtype="bf16")
+    err = _rel(_run(m, "standard", internal="bf16"),
+               _oracle(m.double().numpy(), "standard"))
+    print(f"bf16 internal standard: {err:.3e}")
+    assert err < 1.5e-2
+
+
+def test_parity_per_step_coefficients_and_steps():
+    m = workloads.gaussian((192, 448), seed=23, dtype="fp32")
+    sched = [TUNED, oracle.CLASSIC_ABC, TUNED, (1.5, -0.5, 0.0),
+             oracle.CLASSIC_ABC, oracle.CLASSIC_ABC, TUNED]
+    m64 = m.double().numpy()
+    for mode in ("standard", "gram"):
+        err = _rel(_run(m, mode, steps=7, abc=sched, mask=(1 << 3) | (1 << 6)),
+                   _oracle(m64, mode, steps=7, abc=sched,
+                           mask=(1 << 3) | (1 << 6)))
+        assert err < 1e-4, (mode, err)
+    for steps in (1, 2, 3):
+        err = _rel(_run(m, "gram", steps=steps),
+                   _oracle(m64, "gram", steps=steps))
+        assert err < 1e-4, (steps, err)
+
+
+def test_parity_strided_rows():
+    m = workloads.gaussian((150, 260), seed=24, dtype="bf16")
+    ref = _oracle(m.double().numpy(), "standard")
+    assert _rel(_run(m, "standard", ld_pad=37), ref) < 1e-2
+    mt = workloads.gaussian((260, 150), seed=25, dtype="bf16")
+    ref = _oracle(mt.double().numpy(), "gram")
+    assert _rel(_run(mt, "gram", ld_pad=8), ref) < 1e-2
+
+
+def test_zero_matrix_gives_zero():
+    dev = _dev()
+    for mode in ("standard", "gram"):
+        x = torch.zeros(64, 96, dtype=torch.bfloat16, device=dev)
+        nsa.orthogonalize(x, mode=mode)
+        assert torch.count_nonzero(x).item() == 0
+
+
+def test_nonfinite_status_flag():
+    dev = _dev()
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    x = workloads.gaussian((64, 96), seed=26).to(dev)
+    nsa.orthogonalize(x, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    x = workloads.gaussian((64, 96), seed=26).to(dev)
+    x[3, 5] = float("nan")
+    nsa.orthogonalize(x, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 1
+
+
+def test_exact_symmetry_and_orientation():
+    # The tall result is the transpose of the wide result, bit for bit.
+    dev = _dev()
+    m = workloads.gaussian((180, 420), seed=27, dtype="fp16")
+    for mode in ("standard", "gram"):
+        a = m.to(dev)
+        b = m.t().contiguous().to(dev)
+        nsa.orthogonalize(a, mode=mode)
+        nsa.orthogonalize(b, mode=mode)
+        assert torch.equal(a, b.t())
+
+
+# ---------------------------------------------------------------------------
+# Batched launcher.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(200, 136), (136, 200), (256, 512)])
+@pytest.mark.parametrize("mode", ["gram", "standard"])
+def test_batched_matches_oracle_and_single_calls(shape, mode):
+    dev = _dev()
+    e = 5
+    m = workloads.gaussian((e,) + shape, seed=28, dtype="bf16")
+    x = m.to(dev)
+    nsa.orthogonalize_batched(x, mode=mode)
+    torch.cuda.synchronize()
+    for i in range(e):
+        single = m[i].to(dev)
+        nsa.orthogonalize(single, mode=mode)
+        assert torch.equal(single, x[i]), i
+        err = _rel(x[i].double().cpu().numpy(),
+                   _oracle(m[i].double().numpy(), mode))
+        assert err < 1e-2, (i, err)
+
+
+# ---------------------------------------------------------------------------
+# Soft-threshold split.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("numel_shape", [(1, 1), (3, 5), (64, 96), (333, 77),
+                                         (512, 2048)])
+def test_soft_threshold_matches_oracle(dtype, numel_shape):
+    dev = _dev()
+    m = workloads.student_t(numel_shape, seed=29, dtype=dtype)
+    m64 = m.double().numpy()
+    b_ref, o_ref, lam_ref = oracle.soft_threshold_split(m64)
+    lam_out = torch.zeros(1, dtype=torch.float32, device=dev)
+    b, o = nsa.soft_threshold_split(m.to(dev), lambda_out=lam_out)
+    torch.cuda.synchronize()
+    lam = lam_out.item()
+    # The median is an order statistic of the stored values: exact.
+    med = oracle.lower_median_abs(m64)
+    assert lam == np.float32(3.0 * med) or lam == pytest.approx(3.0 * med,
+                                                                rel=1e-7)
+    b = b.double().cpu().numpy()
+    o = o.double().cpu().numpy()
+    # Which entries are clipped: exact.
+    assert np.array_equal(np.abs(b_ref) >= lam_ref, np.abs(m64) >= lam_ref)
+    clipped_ref = np.abs(m64) > lam_ref
+    assert np.array_equal(o_ref != 0, clipped_ref)
+    assert np.array_equal(b[~clipped_ref], m64[~clipped_ref])
+    # Clipped entries hold lambda rounded to the storage type; O within one
+    # storage ulp of the exact outlier.
+    ulp = {"bf16": 2.0 ** -7, "fp16": 2.0 ** -10, "fp32": 2.0 ** -23}[dtype]
+    assert np.all(np.abs(np.abs(b[clipped_ref]) - lam_ref) <= ulp * lam_ref)
+    assert np.all(np.abs(o - o_ref) <= ulp * (np.abs(o_ref) + lam_ref))
+
+
+def test_soft_threshold_explicit_lambda_and_in_place():
+    dev = _dev()
+    m = workloads.student_t((100, 100), seed=30, dtype="bf16")
+    x = m.to(dev)
+    b, o = nsa.soft_threshold_split(x, lam=1.0, out_b=x)
+    torch.cuda.synchronize()
+    ref_b, ref_o, _ = oracle.soft_threshold_split(m.double().numpy(), lam=1.0)
+    assert np.array_equal(x.double().cpu().numpy(), ref_b)
+    assert np.abs(o.double().cpu().numpy() - ref_o).max() <= 2 ** -7 * (
+        np.abs(ref_o).max() + 1)
