@@ -2,7 +2,7 @@
 
 Default workload: one Llama-8B MLP-shaped matrix, 4096 x 14336 bf16, with
 N(0,1) entries times log-uniform column scales in [1e-3, 1], orthogonalized
-by the Gram form (5 tuned steps, restart before step 3).  A step is one full
+by the Gram form (5 tuned steps, restart before step 4).  A step is one full
 ns_orthogonalize call on a matrix already resident in HBM: norm, staging,
 every product, and the final cast back into the caller's buffer.  The call
 works in place, so each step orthogonalizes the previous step's output; the
@@ -47,7 +47,7 @@ def parse():
                              "moe-experts", "moe-experts-t", "small-fp32"])
     ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
     ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
-    ap.add_argument("--restart-mask", type=int, default=1 << 3)
+    ap.add_argument("--restart-mask", type=int, default=1 << 4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-form companion measurement")

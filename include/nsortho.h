@@ -91,7 +91,7 @@ typedef struct ns_trace {
 typedef struct ns_options {
   /* Gram form only.  Bit k (1 <= k <= steps) set: restart before step k
    * (X <- Q X, R <- X X^T, Q <- I).  0 is the naive Gram iteration.
-   * Default (1u << 3): one restart, before step 3. */
+   * Default (1u << 4): one restart, before step 4. */
   uint32_t restart_mask;
   /* Added to ||X||_F before dividing.  Default 1e-7.  A zero matrix gives a
    * zero result. */

@@ -150,7 +150,7 @@ def dtype_code(dtype: torch.dtype) -> int:
         raise TypeError(f"unsupported dtype {dtype}; use bf16, fp16 or fp32")
 
 
-def make_options(restart_mask: int = 1 << 3, eps: float = 1e-7,
+def make_options(restart_mask: int = 1 << 4, eps: float = 1e-7,
                  internal: Optional[str] = None,
                  status: Optional[torch.Tensor] = None,
                  trace: Optional[Trace] = None) -> Options:
@@ -195,7 +195,7 @@ def _workspace(nbytes: int, device: torch.device,
 
 def workspace_size(rows: int, cols: int, batch: int = 1,
                    dtype: torch.dtype = torch.bfloat16,
-                   mode: str = "standard", restart_mask: int = 1 << 3,
+                   mode: str = "standard", restart_mask: int = 1 << 4,
                    internal: Optional[str] = None) -> int:
     opt = make_options(restart_mask, 1e-7, internal)
     return int(lib().ns_workspace_size(rows, cols, batch, dtype_code(dtype),
@@ -212,7 +212,7 @@ def _check_matrix(x: torch.Tensor, ndim: int) -> None:
 
 
 def orthogonalize(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
-                  mode: str = "standard", restart_mask: int = 1 << 3,
+                  mode: str = "standard", restart_mask: int = 1 << 4,
                   eps: float = 1e-7, internal: Optional[str] = None,
                   status: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None,
@@ -238,7 +238,7 @@ def orthogonalize(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
 
 
 def orthogonalize_batched(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
-                          mode: str = "gram", restart_mask: int = 1 << 3,
+                          mode: str = "gram", restart_mask: int = 1 << 4,
                           eps: float = 1e-7, internal: Optional[str] = None,
                           status: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None,

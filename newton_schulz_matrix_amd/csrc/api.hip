@@ -328,7 +328,7 @@ struct Runner {
       return hipSuccess;
     }
     // Gram form.
-    const uint32_t mask = opt ? opt->restart_mask : (1u << 3);
+    const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
     T* R = nnbuf(0);
     T* Z = nnbuf(1);
     T* Qb[2] = {nnbuf(2), nnbuf(3)};
@@ -401,7 +401,7 @@ ns_status orthogonalize_impl(void* X, int64_t batch, int64_t rows, int64_t cols,
   ns_status s = make_plan(rows, cols, batch, dtype, mode, opt, &p);
   if (s != NS_OK) return s;
   if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
-  const uint32_t mask = opt ? opt->restart_mask : (1u << 3);
+  const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
   if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal)) != NS_OK) return s;
   if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -464,7 +464,7 @@ extern "C" {
 
 void ns_options_default(ns_options* opt) {
   if (!opt) return;
-  opt->restart_mask = 1u << 3;
+  opt->restart_mask = 1u << 4;
   opt->eps = 1e-7f;
   opt->internal = -1;
   opt->d_status = nullptr;

@@ -41,7 +41,7 @@ def standard_flops(n: int, m: int, steps: int = 5,
 
 
 def gram_flops(n: int, m: int, steps: int = 5,
-               restarts: Iterable[int] = (3,),
+               restarts: Iterable[int] = (4,),
                symmetric: bool = True) -> float:
     n, m = min(n, m), max(n, m)
     sym = 1.0 if symmetric else 2.0
@@ -65,7 +65,7 @@ def gram_flops(n: int, m: int, steps: int = 5,
 
 
 def ns_flops(rows: int, cols: int, steps: int = 5, mode: str = "standard",
-             restart_mask: int = 1 << 3, symmetric: bool = True) -> float:
+             restart_mask: int = 1 << 4, symmetric: bool = True) -> float:
     """FLOPs of one orthogonalization of a rows x cols matrix."""
     if mode == "standard":
         return standard_flops(rows, cols, steps, symmetric)

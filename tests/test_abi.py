@@ -54,7 +54,7 @@ def test_status_strings():
 def test_options_defaults():
     opt = B.Options()
     B.lib().ns_options_default(ctypes.byref(opt))
-    assert opt.restart_mask == 1 << 3
+    assert opt.restart_mask == 1 << 4
     assert abs(opt.eps - 1e-7) < 1e-12
     assert opt.internal == -1 and not opt.d_status
 
