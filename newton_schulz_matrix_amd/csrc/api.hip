@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -17,7 +19,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kPrescaleExp16 = 10;  // X is held as 2^10 * X in 16-bit storage
-constexpr int kMaxPartials = 256;
+constexpr int kMaxPartials = 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -36,7 +38,7 @@ struct Plan {
   int partials = 1;
   int nn_count = 2;
   int64_t x_elems = 0, nn_elems = 0;
-  size_t off_partial = 0, off_x[2] = {0, 0}, off_nn[4] = {0, 0, 0, 0}, total = 0;
+  size_t off_partial = 0, off_scale = 0, off_x[2] = {0, 0}, off_nn[4] = {0, 0, 0, 0}, total = 0;
 };
 
 bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
@@ -59,8 +61,9 @@ bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
 }
 
 // Tile edge: 256 when the small side is large and needs no extra padding
-// for it, else 128.
-int pick_tile(int64_t n) {
+// for it (16-bit products only), else 128.
+int pick_tile(int64_t n, ns_dtype internal) {
+  if (internal == NS_FP32) return 128;  // an fp32 256 x 256 tile does not fit in LDS
   if (n >= 512 && round_up(n, 256) == round_up(n, 128)) return 256;
   return 128;
 }
@@ -81,7 +84,7 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
   p->transposed = rows > cols;
   p->n = p->transposed ? cols : rows;
   p->m = p->transposed ? rows : cols;
-  p->tile = pick_tile(p->n);
+  p->tile = pick_tile(p->n, internal);
   p->n_pad = round_up(p->n, p->tile);
   p->m_pad = round_up(p->m, p->tile);
   p->esz = elem_size(internal);
@@ -89,12 +92,15 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
   p->nn_elems = p->n_pad * p->n_pad;
   // Offsets inside one matrix are 32-bit in the kernels' index math.
   if ((double)p->x_elems * p->esz >= 2147483648.0 || p->n_pad > 65536) return NS_ERR_INVALID_ARG;
-  const int64_t want = (p->n + 15) / 16;
-  p->partials = (int)(want < 1 ? 1 : (want > kMaxPartials ? kMaxPartials : want));
+  // About 2048 norm blocks in total, at most one per input row.
+  const int64_t want = (2048 + batch - 1) / batch;
+  p->partials = (int)std::min<int64_t>(std::min<int64_t>(want, rows), kMaxPartials);
   p->nn_count = mode == NS_GRAM ? 4 : 2;
   size_t off = 0;
   p->off_partial = off;
   off = align_up(off + (size_t)batch * p->partials * sizeof(double));
+  p->off_scale = off;
+  off = align_up(off + (size_t)batch * sizeof(float));
   for (int i = 0; i < 2; ++i) {
     p->off_x[i] = off;
     off = align_up(off + (size_t)batch * p->x_elems * p->esz);
@@ -137,24 +143,15 @@ struct Tracer {
 // ---------------------------------------------------------------------------
 template <typename T, int TILE, bool GRAM_INPUT>
 hipError_t launch_sym(const SymArgs<T>& a, int64_t batch, hipStream_t s) {
-  const size_t smem = 4 * (size_t)TILE * kRowBytes;
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym<T, TILE, GRAM_INPUT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (attr != hipSuccess) return attr;
   const int ntri = a.tiles * (a.tiles + 1) / 2;
-  hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT>), dim3(ntri, (unsigned)batch), dim3(kThreads), smem, s, a);
+  hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT>), dim3(ntri, (unsigned)batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename T, typename OutT, int TILE>
 hipError_t launch_nn(const NNArgs<T, OutT>& a, int64_t batch, hipStream_t s) {
-  const size_t smem = 4 * (size_t)TILE * kRowBytes;
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_nn<T, OutT, TILE>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_nn<T, OutT, TILE>), dim3(a.tiles_m * a.tiles_n, (unsigned)batch), dim3(kThreads), smem, s, a);
+  const dim3 grid(a.tiles_m * a.tiles_n, (unsigned)batch);
+  hipLaunchKernelGGL((k_nn<T, OutT, TILE>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -285,17 +282,20 @@ struct Runner {
       return hipGetLastError();
     });
     if (e != hipSuccess) return e;
+    float* scales = reinterpret_cast<float*>(ws + p.off_scale);
+    hipLaunchKernelGGL(k_scale, dim3((unsigned)p.batch), dim3(kStageThreads), 0, st, partial, p.partials, prescale,
+                       eps, scales);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     return tr.run(NS_KERNEL_STAGE, 0.0, elems * (sizeof(IO) + sizeof(T)), [&] {
       if (!p.transposed) {
         hipLaunchKernelGGL((k_stage_rows<IO, T>), dim3((unsigned)p.n_pad, (unsigned)p.batch), dim3(kStageThreads),
-                           0, st, user, p.rows, p.cols, ld, bstride, partial, p.partials, prescale, eps, xbuf(0),
-                           p.m_pad, p.x_elems);
+                           0, st, user, p.rows, p.cols, ld, bstride, scales, xbuf(0), p.m_pad, p.x_elems);
       } else {
         const int tj = (int)(p.m_pad / 64);
         const int ti = (int)(p.n_pad / 64);
         hipLaunchKernelGGL((k_stage_transpose<IO, T>), dim3((unsigned)(ti * tj), (unsigned)p.batch),
-                           dim3(kStageThreads), 0, st, user, p.rows, p.cols, ld, bstride, partial, p.partials,
-                           prescale, eps, xbuf(0), p.m_pad, p.x_elems, tj);
+                           dim3(kStageThreads), 0, st, user, p.rows, p.cols, ld, bstride, scales, xbuf(0), p.m_pad,
+                           p.x_elems, tj);
       }
       return hipGetLastError();
     });
@@ -369,7 +369,12 @@ ns_status run_typed(const Plan& p, void* X, int64_t ld, int64_t bstride, int ste
   Runner<T, IO> r{p, reinterpret_cast<char*>(ws), st, reinterpret_cast<IO*>(X), ld, bstride, opt,
                   Tracer{opt ? opt->trace : nullptr, st}};
   const float eps = opt ? opt->eps : 1e-7f;
-  hipError_t e = (p.tile == 256) ? r.template run<256>(steps, a, b, c, eps) : r.template run<128>(steps, a, b, c, eps);
+  hipError_t e;
+  if constexpr (sizeof(T) == 4) {
+    e = r.template run<128>(steps, a, b, c, eps);
+  } else {
+    e = (p.tile == 256) ? r.template run<256>(steps, a, b, c, eps) : r.template run<128>(steps, a, b, c, eps);
+  }
   return hip_status(e);
 }
 

@@ -43,6 +43,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;  // bytes of one operand row in one k-tile
@@ -118,32 +120,45 @@ template <> __device__ __forceinline__ void mma_chunk<float>(const uint4& a, con
 // Global -> LDS loaders.
 // ---------------------------------------------------------------------------
 
-// K-contiguous operand: TILE rows of 128 bytes per k-tile.
+// K-contiguous operand: TILE rows of 128 bytes per k-tile, copied straight
+// from global memory into LDS (global_load_lds_dwordx4: lane L of a wave
+// writes its 16 bytes at M0 + 16 L).  One instruction fills 8 LDS rows; lane
+// L fetches the chunk that belongs at slot L & 7 of row L >> 3, so the LDS
+// swizzle is applied on the global side.  Row r = 8 q + (L >> 3) of the wave
+// has swz(r) = (L >> 3) ^ (q & 7).
 template <int TILE>
-struct RowLoader {
-  static constexpr int kPer = TILE * 8 / kThreads;  // 16-byte chunks per thread
-  uint4 r[kPer];
-  __device__ __forceinline__ void load(const char* g, int64_t ld_bytes, int kt) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q >> 3, ch = q & 7;
-      r[i] = *reinterpret_cast<const uint4*>(g + (int64_t)row * ld_bytes + (int64_t)kt * kRowBytes + ch * 16);
-    }
+struct DmaLoader {
+  static constexpr int kRowsPerWave = TILE / 4;
+  static constexpr int kIters = kRowsPerWave / 8;
+  uint32_t lane_off;   // (L >> 3) * ld + 16 * ((L & 7) ^ (L >> 3))
+  uint32_t ld8;        // 8 * ld (bytes), uniform
+  int wave_row0;       // first LDS row this wave fills (uniform)
+  __device__ __forceinline__ void init(int64_t ld_bytes) {
+    const int lane = threadIdx.x & 63;
+    wave_row0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kRowsPerWave;
+    lane_off = (uint32_t)((lane >> 3) * ld_bytes) + (uint32_t)((((lane & 7) ^ (lane >> 3))) << 4);
+    ld8 = (uint32_t)(8 * ld_bytes);
   }
-  __device__ __forceinline__ void store(char* s) const {
+  // g: operand tile base (rows of this tile), kt: k-tile, lds_op: LDS base
+  // of the operand in the stage being filled.
+  __device__ __forceinline__ void issue(const char* g, int kt, char* lds_op) const {
+    const char* gw = g + (int64_t)wave_row0 * (ld8 >> 3) + (int64_t)kt * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q >> 3, ch = q & 7;
-      *reinterpret_cast<uint4*>(s + lds_off(row, ch)) = r[i];
+    for (int i = 0; i < kIters; ++i) {
+      const int q = (wave_row0 >> 3) + i;  // LDS row group, uniform
+      const uint32_t off = lane_off + (uint32_t)i * ld8;
+      // The chunk XOR for this row group: (q & 7) applied to the low bits.
+      const uint32_t sw = (uint32_t)((q & 7) << 4);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gw + (off ^ sw)),
+                                       (lds_void_t*)(lds_op + q * 8 * kRowBytes), 16, 0, 0);
     }
   }
 };
 
 // X operand of nn: k runs along X's rows.  A k-tile is BK rows x TILE
 // columns of X; it is stored in LDS as TILE rows (one per column of X) of
-// BK k-values, by transposing E x E blocks in registers.
+// BK k-values, by transposing E x E blocks in registers.  Thread t owns
+// column block jb = t % JB and k block kb = t / JB.
 template <typename T, int TILE>
 struct ColLoader {
   static constexpr int E = 16 / sizeof(T);        // elements per chunk
@@ -153,14 +168,16 @@ struct ColLoader {
   static constexpr int kPer = (NBLK + kThreads - 1) / kThreads;
   uint4 r[kPer][E];
   __device__ __forceinline__ void load(const char* g, int64_t ld_bytes, int kt) {
+    const char* gk = g + (int64_t)kt * BK * ld_bytes;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int b = threadIdx.x + i * kThreads;
       if (NBLK % kThreads == 0 || b < NBLK) {
         const int jb = b % JB, kb = b / JB;
-        const char* p = g + ((int64_t)kt * BK + kb * E) * ld_bytes + jb * 16;
+        const uint32_t off = (uint32_t)(kb * E * ld_bytes) + (uint32_t)(jb * 16);
 #pragma unroll
-        for (int rr = 0; rr < E; ++rr) r[i][rr] = *reinterpret_cast<const uint4*>(p + rr * ld_bytes);
+        for (int rr = 0; rr < E; ++rr)
+          r[i][rr] = *reinterpret_cast<const uint4*>(gk + (off + (uint32_t)(rr * ld_bytes)));
       }
     }
   }
@@ -170,10 +187,13 @@ struct ColLoader {
       const int b = threadIdx.x + i * kThreads;
       if (NBLK % kThreads == 0 || b < NBLK) {
         const int jb = b % JB, kb = b / JB;
+        // Row j = jb*E + jj; for E == 8, swz(j) = jj ^ (jb & 7).
+        const uint32_t* in = reinterpret_cast<const uint32_t*>(&r[i][0]);
         if constexpr (E == 8) {
           // 8 x 8 block of 16-bit values: in[rr].dword[d] = (col 2d, col 2d+1)
           // of k-row rr; out[jj].dword[e] = (k 2e, k 2e+1) of column jj.
-          const uint32_t* in = reinterpret_cast<const uint32_t*>(&r[i][0]);
+          char* base = s + jb * 8 * kRowBytes;
+          const int x = kb ^ (jb & 7);
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
             uint32_t o[4];
@@ -183,11 +203,10 @@ struct ColLoader {
               const uint32_t hi = in[(2 * e + 1) * 4 + (jj >> 1)];
               o[e] = (jj & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
             }
-            *reinterpret_cast<uint4*>(s + lds_off(jb * 8 + jj, kb)) = uint4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<uint4*>(base + jj * kRowBytes + ((x ^ jj) << 4)) = uint4{o[0], o[1], o[2], o[3]};
           }
         } else {
           // 4 x 4 block of fp32 values.
-          const uint32_t* in = reinterpret_cast<const uint32_t*>(&r[i][0]);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             *reinterpret_cast<uint4*>(s + lds_off(jb * 4 + jj, kb)) =
@@ -200,77 +219,185 @@ struct ColLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Main loop: acc[fm][fn] += L-tile * R-tile^T over `ktiles` k-tiles.
-// sL/sR layout per stage: TILE rows x 128 bytes each.
+// Main loop: acc[fm][fn] += L-tile * R-tile^T over a range of k-tiles.
 // ---------------------------------------------------------------------------
+template <int FM>
+struct Frags {
+  uint4 a[FM], b[FM];
+};
+
+// Per-lane LDS byte offsets of this wave's fragment rows.  Fragment i of a
+// wave covers rows w0 + 32 i + (L & 31) with w0 a multiple of 64, so
+// swz(row) = (L & 7) ^ (4 (i & 1) + ((L & 31) >> 3)) only depends on the
+// parity of i; the offset of (i, chunk c) is row0 + 4096 i + 16 (c ^ swz).
+struct FragAddr {
+  uint32_t row0L, row0R;  // (w0 + (L & 31)) * 128 for the L and R operands
+  int sw0, sw1;           // swz for even and odd i
+  __device__ __forceinline__ void init(int wr, int wc) {
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 31;
+    row0L = (uint32_t)((wr + lr) * kRowBytes);
+    row0R = (uint32_t)((wc + lr) * kRowBytes);
+    sw0 = (lr & 7) ^ (lr >> 3);
+    sw1 = (lr & 7) ^ (4 + (lr >> 3));
+  }
+};
+
+// Fragments of substep s (16-byte chunk pair 2s, 2s+1) for this wave.
+template <int FM>
+__device__ __forceinline__ void load_frags(const char* sL, const char* sR, const FragAddr& fa, int s,
+                                           Frags<FM>& f) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const uint32_t c0 = (uint32_t)(((2 * s + h) ^ fa.sw0) << 4);
+  const uint32_t c1 = (uint32_t)(((2 * s + h) ^ fa.sw1) << 4);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    f.a[i] = *reinterpret_cast<const uint4*>(sR + (fa.row0R + ((i & 1) ? c1 : c0)) + i * 32 * kRowBytes);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    f.b[i] = *reinterpret_cast<const uint4*>(sL + (fa.row0L + ((i & 1) ? c1 : c0)) + i * 32 * kRowBytes);
+}
+
+template <typename T, int FM>
+__device__ __forceinline__ void mma_frags(const Frags<FM>& f, f32x16 (&acc)[FM][FM]) {
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FM; ++fn) mma_chunk<T>(f.a[fn], f.b[fm], acc[fm][fn]);
+}
+
+// All four substeps of one k-tile, with the fragments of substep s+1 read
+// from LDS while the MFMAs of substep s run.  `mid` runs between substeps 1
+// and 2 (the nn kernel stores its transposed operand there).
+template <typename T, int TILE, class Mid>
+__device__ __forceinline__ void compute_ktile(const char* sL, const char* sR, const FragAddr& fa,
+                                              f32x16 (&acc)[TILE / 64][TILE / 64], Mid&& mid) {
+  constexpr int FM = TILE / 64;
+  Frags<FM> f0, f1;
+  load_frags<FM>(sL, sR, fa, 0, f0);
+  load_frags<FM>(sL, sR, fa, 1, f1);
+  mma_frags<T, FM>(f0, acc);
+  load_frags<FM>(sL, sR, fa, 2, f0);
+  mma_frags<T, FM>(f1, acc);
+  mid();
+  load_frags<FM>(sL, sR, fa, 3, f1);
+  mma_frags<T, FM>(f0, acc);
+  mma_frags<T, FM>(f1, acc);
+}
+
+// Instruction order for a k-tile of the DMA path (one basic block): the
+// global->LDS copies of the next k-tile first, the fragment reads of
+// substeps 0 and 1, then the reads of substeps 2 and 3 spread between the
+// MFMAs of substeps 0 and 1, then the MFMAs of substeps 2 and 3.  The MFMA
+// count per 16-byte chunk is 1 (16-bit) or 4 (fp32).
+template <typename T, int TILE>
+__device__ __forceinline__ void schedule_dma_ktile() {
+  constexpr int FM = TILE / 64;
+  constexpr int NR = 2 * FM;                                   // reads per substep
+  constexpr int NM = FM * FM * (sizeof(T) == 4 ? 4 : 1);       // MFMAs per substep
+  __builtin_amdgcn_sched_group_barrier(0x020, 2 * (TILE / 32), 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);
+}
+
 template <typename T, int TILE>
 struct Acc {
   static constexpr int FM = TILE / 64;  // 32x32 MFMA tiles per wave per dim
   f32x16 v[FM][FM];
 };
 
-template <typename T, int TILE>
-__device__ __forceinline__ void compute_ktile(const char* sL, const char* sR, int wr, int wc, Acc<T, TILE>& acc) {
-  constexpr int FM = Acc<T, TILE>::FM;
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint4 a[FM], b[FM];
-#pragma unroll
-    for (int f = 0; f < FM; ++f) a[f] = *reinterpret_cast<const uint4*>(sR + lds_off(wc + f * 32 + lr, 2 * s + h));
-#pragma unroll
-    for (int f = 0; f < FM; ++f) b[f] = *reinterpret_cast<const uint4*>(sL + lds_off(wr + f * 32 + lr, 2 * s + h));
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FM; ++fn) mma_chunk<T>(a[fn], b[fm], acc.v[fm][fn]);
+// The two LDS stages are distinct __shared__ objects (per tile size), so the
+// compiler can tell the DMA writes into one stage from the fragment reads of
+// the other and does not wait for the loads in flight before every read.
+// Each stage holds the L operand (TILE rows x 128 bytes) followed by the R
+// operand.
+__shared__ __attribute__((aligned(1024))) char g_stage0_256[2 * 256 * kRowBytes];
+__shared__ __attribute__((aligned(1024))) char g_stage1_256[2 * 256 * kRowBytes];
+__shared__ __attribute__((aligned(1024))) char g_stage0_128[2 * 128 * kRowBytes];
+__shared__ __attribute__((aligned(1024))) char g_stage1_128[2 * 128 * kRowBytes];
+
+template <int TILE> struct Stages;
+template <> struct Stages<256> {
+  static __device__ __forceinline__ char* s0() { return g_stage0_256; }
+  static __device__ __forceinline__ char* s1() { return g_stage1_256; }
+};
+template <> struct Stages<128> {
+  static __device__ __forceinline__ char* s0() { return g_stage0_128; }
+  static __device__ __forceinline__ char* s1() { return g_stage1_128; }
+};
+
+// One k-tile: start the loads of k-tile kt+1 into `nxt` (when there is one),
+// run the MFMAs on `cur`, then wait for the loads and synchronize.
+template <typename T, int TILE, bool COL_RIGHT>
+__device__ __forceinline__ void ktile_step(const char* Lg, const char* Rg, int64_t ldr_bytes,
+                                           const DmaLoader<TILE>& la, const DmaLoader<TILE>& lb, int kt,
+                                           bool more, const char* __restrict__ cur, char* __restrict__ nxt,
+                                           const FragAddr& fa,
+                                           f32x16 (&acc)[TILE / 64][TILE / 64]) {
+  constexpr int kOpBytes = TILE * kRowBytes;
+  if constexpr (COL_RIGHT) {
+    ColLoader<T, TILE> cb;
+    if (more) {
+      la.issue(Lg, kt + 1, nxt);
+      cb.load(Rg, ldr_bytes, kt + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute_ktile<T, TILE>(cur, cur + kOpBytes, fa, acc, [&] {
+      if (more) cb.store(nxt + kOpBytes);
+    });
+  } else {
+    // Always copy: the last k-tile reloads itself into the idle stage, so
+    // the step is one basic block the schedule below can order.
+    const int ktn = more ? kt + 1 : kt;
+    la.issue(Lg, ktn, nxt);
+    lb.issue(Rg, ktn, nxt + kOpBytes);
+    compute_ktile<T, TILE>(cur, cur + kOpBytes, fa, acc, [] {});
+    schedule_dma_ktile<T, TILE>();
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
+// acc += L-tile * R-tile^T over k-tiles [kt0, kt1) (acc is initialized by the
+// caller).
 template <typename T, int TILE, bool COL_RIGHT>
 __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, const char* Rg, int64_t ldr_bytes,
-                                         int ktiles, char* smem, Acc<T, TILE>& acc) {
-  constexpr int FM = Acc<T, TILE>::FM;
+                                         int kt0, int kt1, Acc<T, TILE>& acc) {
   constexpr int kOpBytes = TILE * kRowBytes;
-  // Stage s: L operand at smem + 2*s*kOpBytes, R operand right after it.
   const int w = threadIdx.x >> 6;
   const int wr = (w >> 1) * (TILE / 2), wc = (w & 1) * (TILE / 2);
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < FM; ++fn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc.v[fm][fn][v] = 0.f;
+  if (kt1 <= kt0) return;
 
-  using RightLoader = typename std::conditional<COL_RIGHT, ColLoader<T, TILE>, RowLoader<TILE>>::type;
-  {
-    RowLoader<TILE> la;
-    RightLoader lb;
-    la.load(Lg, ldl_bytes, 0);
-    lb.load(Rg, ldr_bytes, 0);
-    la.store(smem);
-    lb.store(smem + kOpBytes);
+  char* s0 = Stages<TILE>::s0();
+  char* s1 = Stages<TILE>::s1();
+  FragAddr fa;
+  fa.init(wr, wc);
+  DmaLoader<TILE> la, lb;
+  la.init(ldl_bytes);
+  if constexpr (!COL_RIGHT) lb.init(ldr_bytes);
+
+  la.issue(Lg, kt0, s0);
+  if constexpr (COL_RIGHT) {
+    ColLoader<T, TILE> cb;
+    cb.load(Rg, ldr_bytes, kt0);
+    cb.store(s0 + kOpBytes);
+  } else {
+    lb.issue(Rg, kt0, s0 + kOpBytes);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // The loaders live inside one iteration so their registers are never
-  // carried around the loop; the last k-tile is peeled.
-  for (int kt = 0; kt + 1 < ktiles; ++kt) {
-    const int cur = kt & 1;
-    RowLoader<TILE> la;
-    RightLoader lb;
-    la.load(Lg, ldl_bytes, kt + 1);
-    lb.load(Rg, ldr_bytes, kt + 1);
-    const char* sc = smem + cur * 2 * kOpBytes;
-    compute_ktile<T, TILE>(sc, sc + kOpBytes, wr, wc, acc);
-    char* sn = smem + (cur ^ 1) * 2 * kOpBytes;
-    la.store(sn);
-    lb.store(sn + kOpBytes);
-    __syncthreads();
-  }
-  {
-    const char* sc = smem + ((ktiles - 1) & 1) * 2 * kOpBytes;
-    compute_ktile<T, TILE>(sc, sc + kOpBytes, wr, wc, acc);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const bool odd = (kt - kt0) & 1;
+    ktile_step<T, TILE, COL_RIGHT>(Lg, Rg, ldr_bytes, la, lb, kt, kt + 1 < kt1, odd ? s1 : s0, odd ? s0 : s1, fa,
+                                   acc.v);
   }
 }
 
@@ -324,12 +451,50 @@ __device__ __forceinline__ void tri_tile(int idx, int tiles, int& tm, int& tn) {
   tn = r + left;
 }
 
+// Output tile staged in LDS (the stage buffers are free after the main
+// loop): TILE rows of TILE * sizeof(T) bytes, 16-byte chunk q of row r at
+// slot q ^ tswz(r).  The swizzle keeps both the row-quad writes from the
+// accumulators (32 consecutive rows) and the column reads of the mirrored
+// store (rows 8 apart) on distinct chunks.
+// The tile spans the two stage buffers: rows [0, kRowsPerStage) in the
+// first, the rest in the second.
+template <typename T, int TILE>
+struct TileLds {
+  static constexpr int kRowB = TILE * (int)sizeof(T);
+  static constexpr int kCPR = kRowB / 16;          // chunks per row
+  static constexpr int kEC = 16 / (int)sizeof(T);  // elements per chunk
+  static constexpr int kS = kCPR == 32 ? 5 : 4;
+  static constexpr int kStageB = 2 * TILE * kRowBytes;
+  static constexpr int kRowsPerStage = kStageB / kRowB;
+  static_assert(kCPR == 32 || kCPR == 16, "tile row must be 256 or 512 bytes");
+  static_assert(TILE <= 2 * kRowsPerStage, "tile must fit in the two stage buffers");
+  static __device__ __forceinline__ int tswz(int r) { return (r ^ (r >> kS)) & (kCPR - 1); }
+  static __device__ __forceinline__ char* row_base(int r) {
+    return r < kRowsPerStage ? Stages<TILE>::s0() + r * kRowB : Stages<TILE>::s1() + (r - kRowsPerStage) * kRowB;
+  }
+  static __device__ __forceinline__ char* at(int r, int col) {
+    return row_base(r) + (((col / kEC) ^ tswz(r)) << 4) + (col % kEC) * (int)sizeof(T);
+  }
+  static __device__ __forceinline__ char* chunk(int r, int c) { return row_base(r) + ((c ^ tswz(r)) << 4); }
+};
+
+template <typename T, int TILE>
+__device__ __forceinline__ void acc_zero(Acc<T, TILE>& acc) {
+  constexpr int FM = Acc<T, TILE>::FM;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FM; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.v[fm][fn][v] = 0.f;
+}
+
 // GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
 // n x n products into their own kernel symbol, so profiles list them apart.
 template <typename T, int TILE, bool GRAM_INPUT>
 __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int FM = Acc<T, TILE>::FM;
+  using TL = TileLds<T, TILE>;
   int tm, tn;
   tri_tile(blockIdx.x, p.tiles, tm, tn);
   const int bz = blockIdx.y;
@@ -337,73 +502,100 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
   const char* Lg = reinterpret_cast<const char*>(p.L + bz * p.sL) + (int64_t)tm * TILE * ldk_bytes;
   const char* Rg = reinterpret_cast<const char*>(p.R + bz * p.sR) + (int64_t)tn * TILE * ldk_bytes;
   constexpr int BK = kRowBytes / sizeof(T);
-  Acc<T, TILE> acc;
-  mainloop<T, TILE, false>(Lg, ldk_bytes, Rg, ldk_bytes, p.K / BK, smem, acc);
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lr = lane & 31, h = lane >> 5;
-  const int wr = (w >> 1) * (TILE / 2), wc = (w & 1) * (TILE / 2);
   const T* E = p.E ? p.E + bz * p.sE : nullptr;
   T* C = p.C + bz * p.sC;
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
   const bool diag_tile = (tm == tn);
+  const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  Acc<T, TILE> acc;
+  acc_zero<T, TILE>(acc);
+  mainloop<T, TILE, false>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 31, h = lane >> 5;
+  const int wr = (w >> 1) * (TILE / 2), wc = (w & 1) * (TILE / 2);
+
+  // Phase A: beta*E + gamma*acc, rounded to T, into the LDS tile.  The
+  // diagonal of C2 (= C + delta I on real rows) is written here, rounded
+  // once from fp32.
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const int i = tm * TILE + wr + fm * 32 + lr;
+    const int il = wr + fm * 32 + lr;
 #pragma unroll
     for (int fn = 0; fn < FM; ++fn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int j0 = tn * TILE + wc + fn * 32 + 8 * g + 4 * h;
+        const int jl = wc + fn * 32 + 8 * g + 4 * h;
         f32x4 v;
         v[0] = p.gamma * acc.v[fm][fn][4 * g + 0];
         v[1] = p.gamma * acc.v[fm][fn][4 * g + 1];
         v[2] = p.gamma * acc.v[fm][fn][4 * g + 2];
         v[3] = p.gamma * acc.v[fm][fn][4 * g + 3];
-        if (E) {
-          const f32x4 e = Quad<T>::load(E + (int64_t)i * p.ldn + j0);
-          v += p.beta * e;
-        }
-        f32x4 v2 = v;
-        if (C2) {
+        if (E) v += p.beta * Quad<T>::load(E + (row0 + il) * p.ldn + col0 + jl);
+        Quad<T>::store(reinterpret_cast<T*>(TL::at(il, jl)), v);
+        if (C2 && diag_tile) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (i == j0 + e && i < p.n_real) v2[e] += p.delta;
-        }
-        if (!diag_tile) {
-          Quad<T>::store(C + (int64_t)i * p.ldn + j0, v);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) C[(int64_t)(j0 + e) * p.ldn + i] = from_f32<T>(v[e]);
-          if (C2) {
-            Quad<T>::store(C2 + (int64_t)i * p.ldn + j0, v2);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) C2[(int64_t)(j0 + e) * p.ldn + i] = from_f32<T>(v2[e]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = j0 + e;
-            if (i <= j) {
-              const T x = from_f32<T>(v[e]);
-              C[(int64_t)i * p.ldn + j] = x;
-              C[(int64_t)j * p.ldn + i] = x;
-              if (C2) {
-                const T x2 = from_f32<T>(v2[e]);
-                C2[(int64_t)i * p.ldn + j] = x2;
-                C2[(int64_t)j * p.ldn + i] = x2;
-              }
-            }
-          }
+            if (il == jl + e && row0 + il < p.n_real)
+              C2[(row0 + il) * p.ldn + col0 + il] = from_f32<T>(v[e] + p.delta);
         }
       }
     }
+  }
+  __syncthreads();
+
+  // Phase B: rows of the tile.  On a diagonal tile each element (r, j) is
+  // taken from the upper triangle, tile[min(r, j)][max(r, j)], so the result
+  // is exactly symmetric; C2's diagonal was written in phase A.
+  constexpr int kChunks = TILE * TL::kCPR;
+  constexpr int EC = TL::kEC;
+  for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+    const int r = q / TL::kCPR, c = q % TL::kCPR;
+    T* dst = C + (row0 + r) * p.ldn + col0 + c * EC;
+    T* dst2 = C2 ? C2 + (row0 + r) * p.ldn + col0 + c * EC : nullptr;
+    if (!diag_tile) {
+      const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
+      *reinterpret_cast<uint4*>(dst) = val;
+      if (dst2) *reinterpret_cast<uint4*>(dst2) = val;
+    } else {
+      T vals[EC];
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        const int j = c * EC + e;
+        vals[e] = *reinterpret_cast<const T*>(j >= r ? TL::at(r, j) : TL::at(j, r));
+      }
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
+      if (dst2) {
+        const int jd = r - c * EC;  // position of the diagonal inside this chunk
+        if (jd >= 0 && jd < EC && row0 + r < p.n_real) {
+#pragma unroll
+          for (int e = 0; e < EC; ++e)
+            if (e != jd) dst2[e] = vals[e];
+        } else {
+          *reinterpret_cast<uint4*>(dst2) = *reinterpret_cast<const uint4*>(vals);
+        }
+      }
+    }
+  }
+  if (diag_tile) return;
+
+  // Phase C: the mirrored tile, C[col0 + jj][row0 + i] = tile[i][jj]; row jj
+  // of the mirror is column jj of the LDS tile.
+  for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+    const int jj = q / TL::kCPR, c = q % TL::kCPR;
+    T vals[EC];
+#pragma unroll
+    for (int e = 0; e < EC; ++e) vals[e] = *reinterpret_cast<const T*>(TL::at(c * EC + e, jj));
+    const uint4 val = *reinterpret_cast<const uint4*>(vals);
+    *reinterpret_cast<uint4*>(C + (col0 + jj) * p.ldn + row0 + c * EC) = val;
+    if (C2) *reinterpret_cast<uint4*>(C2 + (col0 + jj) * p.ldn + row0 + c * EC) = val;
   }
 }
 
 template <typename T, typename OutT, int TILE>
 __global__ void __launch_bounds__(kThreads, 1) k_nn(NNArgs<T, OutT> p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int FM = Acc<T, TILE>::FM;
+  using TL = TileLds<OutT, TILE>;
   const int tm = blockIdx.x / p.tiles_n;
   const int tn = blockIdx.x % p.tiles_n;
   const int bz = blockIdx.y;
@@ -412,51 +604,85 @@ __global__ void __launch_bounds__(kThreads, 1) k_nn(NNArgs<T, OutT> p) {
   const char* Lg = reinterpret_cast<const char*>(p.B + bz * p.sB) + (int64_t)tm * TILE * ldb_bytes;
   const char* Rg = reinterpret_cast<const char*>(p.X + bz * p.sX) + (int64_t)tn * TILE * sizeof(T);
   constexpr int BK = kRowBytes / sizeof(T);
+  const T* E = p.E ? p.E + bz * p.sE : nullptr;
+  OutT* Y = p.Y + bz * p.sY;
+  const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   Acc<T, TILE> acc;
-  mainloop<T, TILE, true>(Lg, ldb_bytes, Rg, ldx_bytes, p.K / BK, smem, acc);
+  acc_zero<T, TILE>(acc);
+  mainloop<T, TILE, true>(Lg, ldb_bytes, Rg, ldx_bytes, 0, p.K / BK, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
   const int wr = (w >> 1) * (TILE / 2), wc = (w & 1) * (TILE / 2);
-  const T* E = p.E ? p.E + bz * p.sE : nullptr;
-  OutT* Y = p.Y + bz * p.sY;
+  const float scale = p.final_out ? p.out_scale : 1.f;
   bool bad = false;
+
+  // Phase A: alpha*E + gamma*acc (times the output scale), rounded to OutT,
+  // into the LDS tile.
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const int i = tm * TILE + wr + fm * 32 + lr;
+    const int il = wr + fm * 32 + lr;
 #pragma unroll
     for (int fn = 0; fn < FM; ++fn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int j0 = tn * TILE + wc + fn * 32 + 8 * g + 4 * h;
+        const int jl = wc + fn * 32 + 8 * g + 4 * h;
         f32x4 v;
         v[0] = p.gamma * acc.v[fm][fn][4 * g + 0];
         v[1] = p.gamma * acc.v[fm][fn][4 * g + 1];
         v[2] = p.gamma * acc.v[fm][fn][4 * g + 2];
         v[3] = p.gamma * acc.v[fm][fn][4 * g + 3];
-        if (E) {
-          const f32x4 e = Quad<T>::load(E + (int64_t)i * p.ldx + j0);
-          v += p.alpha * e;
-        }
-        if (!p.final_out) {
-          Quad<OutT>::store(Y + (int64_t)i * p.ldy + j0, v);
-        } else {
-          v *= p.out_scale;
-          if (i < p.n_real) {
+        if (E) v += p.alpha * Quad<T>::load(E + (row0 + il) * p.ldx + col0 + jl);
+        v *= scale;
+        if (p.final_out) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int j = j0 + e;
-              if (j < p.m_real) {
-                const OutT x = from_f32<OutT>(v[e]);
-                bad |= !__builtin_isfinite(to_f32<OutT>(x));
-                if (p.transpose_out)
-                  Y[(int64_t)j * p.ldy + i] = x;
-                else
-                  Y[(int64_t)i * p.ldy + j] = x;
-              }
-            }
-          }
+          for (int e = 0; e < 4; ++e) bad |= !__builtin_isfinite(to_f32<OutT>(from_f32<OutT>(v[e])));
         }
+        Quad<OutT>::store(reinterpret_cast<OutT*>(TL::at(il, jl)), v);
+      }
+    }
+  }
+  __syncthreads();
+
+  constexpr int kChunks = TILE * TL::kCPR;
+  if (!p.final_out) {
+    // Internal buffer: whole padded tile, rows of 16-byte chunks.
+    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+      const int r = q / TL::kCPR, c = q % TL::kCPR;
+      *reinterpret_cast<uint4*>(Y + (row0 + r) * p.ldy + col0 + c * TL::kEC) =
+          *reinterpret_cast<const uint4*>(TL::chunk(r, c));
+    }
+  } else if (!p.transpose_out) {
+    // Caller's matrix, same orientation: rows i < n_real, columns j < m_real.
+    const bool vec = (p.ldy % TL::kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+      const int r = q / TL::kCPR, c = q % TL::kCPR;
+      const int64_t i = row0 + r, j0 = col0 + c * TL::kEC;
+      if (i >= p.n_real || j0 >= p.m_real) continue;
+      const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
+      OutT* dst = Y + i * p.ldy + j0;
+      if (vec && j0 + TL::kEC <= p.m_real) {
+        *reinterpret_cast<uint4*>(dst) = val;
+      } else {
+        const OutT* vals = reinterpret_cast<const OutT*>(&val);
+        for (int e = 0; e < TL::kEC && j0 + e < p.m_real; ++e) dst[e] = vals[e];
+      }
+    }
+  } else {
+    // Caller's matrix is the transpose: its row j holds tile column j.
+    const bool vec = (p.ldy % TL::kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+      const int jj = q / TL::kCPR, c = q % TL::kCPR;
+      const int64_t j = col0 + jj, i0 = row0 + c * TL::kEC;
+      if (j >= p.m_real || i0 >= p.n_real) continue;
+      OutT vals[TL::kEC];
+#pragma unroll
+      for (int e = 0; e < TL::kEC; ++e) vals[e] = *reinterpret_cast<const OutT*>(TL::at(c * TL::kEC + e, jj));
+      OutT* dst = Y + j * p.ldy + i0;
+      if (vec && i0 + TL::kEC <= p.n_real) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
+      } else {
+        for (int e = 0; e < TL::kEC && i0 + e < p.n_real; ++e) dst[e] = vals[e];
       }
     }
   }

@@ -35,25 +35,43 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
 }
 
 // partial[b * P + blockIdx.x] = sum of squares over rows blockIdx.x,
-// blockIdx.x + P, ... of matrix b (accumulated in fp64).
+// blockIdx.x + P, ... of matrix b (accumulated in fp64).  The vector path
+// keeps four independent 16-byte loads in flight per thread.
 template <typename IO>
 __global__ void __launch_bounds__(kStageThreads) k_sumsq(const IO* M, int64_t rows, int64_t cols, int64_t ld,
                                                         int64_t bstride, int vec_ok, double* partial, int P) {
   __shared__ double sh[kStageThreads / 64];
   const IO* A = M + (int64_t)blockIdx.y * bstride;
-  double s = 0.0;
+  double s0 = 0.0, s1 = 0.0;
   constexpr int V = 16 / sizeof(IO);
   if (vec_ok) {
     const int64_t cv = cols / V;
     for (int64_t r = blockIdx.x; r < rows; r += P) {
       const uint4* row = reinterpret_cast<const uint4*>(A + r * ld);
-      for (int64_t c = threadIdx.x; c < cv; c += kStageThreads) {
+      int64_t c = threadIdx.x;
+      for (; c + 3 * kStageThreads < cv; c += 4 * kStageThreads) {
+        uint4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = row[c + u * kStageThreads];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const IO* e = reinterpret_cast<const IO*>(&q[u]);
+          float f = 0.f;
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            const float x = to_f32<IO>(e[k]);
+            f = fmaf(x, x, f);
+          }
+          if (u & 1) s1 += (double)f; else s0 += (double)f;
+        }
+      }
+      for (; c < cv; c += kStageThreads) {
         const uint4 q = row[c];
         const IO* e = reinterpret_cast<const IO*>(&q);
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-          const float x = to_f32<IO>(e[k]);
-          s += (double)x * (double)x;
+          const double x = (double)to_f32<IO>(e[k]);
+          s0 += x * x;
         }
       }
     }
@@ -61,21 +79,25 @@ __global__ void __launch_bounds__(kStageThreads) k_sumsq(const IO* M, int64_t ro
     for (int64_t r = blockIdx.x; r < rows; r += P) {
       const IO* row = A + r * ld;
       for (int64_t c = threadIdx.x; c < cols; c += kStageThreads) {
-        const float x = to_f32<IO>(row[c]);
-        s += (double)x * (double)x;
+        const double x = (double)to_f32<IO>(row[c]);
+        s0 += x * x;
       }
     }
   }
-  s = block_sum(s, sh);
-  if (threadIdx.x == 0) partial[(int64_t)blockIdx.y * P + blockIdx.x] = s;
+  const double t = block_sum(s0 + s1, sh);
+  if (threadIdx.x == 0) partial[(int64_t)blockIdx.y * P + blockIdx.x] = t;
 }
 
-// scale = prescale / (sqrt(sum partial) + eps), summed in a fixed order.
-__device__ __forceinline__ float matrix_scale(const double* partial, int P, float prescale, float eps, double* sh) {
+// scale[b] = prescale / (sqrt(sum of the P partials of matrix b) + eps),
+// summed in a fixed order.  One block per matrix.
+__global__ void __launch_bounds__(kStageThreads) k_scale(const double* partial, int P, float prescale, float eps,
+                                                        float* scale) {
+  __shared__ double sh[kStageThreads / 64];
+  const double* pp = partial + (int64_t)blockIdx.x * P;
   double v = 0.0;
-  for (int i = threadIdx.x; i < P; i += kStageThreads) v += partial[i];
+  for (int i = threadIdx.x; i < P; i += kStageThreads) v += pp[i];
   v = block_sum(v, sh);
-  return (float)((double)prescale / (sqrt(v) + (double)eps));
+  if (threadIdx.x == 0) scale[blockIdx.x] = (float)((double)prescale / (sqrt(v) + (double)eps));
 }
 
 // Wide orientation, no transpose: X[i][j] = scale * M[i][j] for i < rows,
@@ -83,12 +105,10 @@ __device__ __forceinline__ float matrix_scale(const double* partial, int P, floa
 // output row; each thread writes 16-byte groups.
 template <typename IO, typename T>
 __global__ void __launch_bounds__(kStageThreads) k_stage_rows(const IO* M, int64_t rows, int64_t cols, int64_t ld,
-                                                             int64_t bstride, const double* partial, int P,
-                                                             float prescale, float eps, T* X, int64_t m_pad,
-                                                             int64_t xstride) {
-  __shared__ double sh[kStageThreads / 64];
+                                                             int64_t bstride, const float* scales, T* X,
+                                                             int64_t m_pad, int64_t xstride) {
   const int b = blockIdx.y;
-  const float scale = matrix_scale(partial + (int64_t)b * P, P, prescale, eps, sh);
+  const float scale = scales[b];
   const int64_t i = blockIdx.x;
   const IO* src = M + (int64_t)b * bstride + i * ld;
   T* dst = X + (int64_t)b * xstride + i * m_pad;
@@ -109,13 +129,11 @@ __global__ void __launch_bounds__(kStageThreads) k_stage_rows(const IO* M, int64
 // LDS tile so both the read of M and the write of X are coalesced.
 template <typename IO, typename T>
 __global__ void __launch_bounds__(kStageThreads) k_stage_transpose(const IO* M, int64_t rows, int64_t cols, int64_t ld,
-                                                                  int64_t bstride, const double* partial, int P,
-                                                                  float prescale, float eps, T* X, int64_t m_pad,
-                                                                  int64_t xstride, int tiles_j) {
-  __shared__ double sh[kStageThreads / 64];
+                                                                  int64_t bstride, const float* scales, T* X,
+                                                                  int64_t m_pad, int64_t xstride, int tiles_j) {
   __shared__ float tile[64][65];
   const int b = blockIdx.y;
-  const float scale = matrix_scale(partial + (int64_t)b * P, P, prescale, eps, sh);
+  const float scale = scales[b];
   const int64_t i0 = (int64_t)(blockIdx.x / tiles_j) * 64;  // X rows  = M cols
   const int64_t j0 = (int64_t)(blockIdx.x % tiles_j) * 64;  // X cols  = M rows
   const IO* src = M + (int64_t)b * bstride;

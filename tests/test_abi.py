@@ -64,7 +64,7 @@ def test_workspace_size_layout():
     ws = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "standard")
     x = 4096 * 14336 * 2
     nn = 4096 * 4096 * 2
-    assert 2 * x + 2 * nn <= ws <= 2 * x + 2 * nn + 4096
+    assert 2 * x + 2 * nn <= ws <= 2 * x + 2 * nn + 16384
     wg = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "gram")
     assert wg - ws == pytest.approx(2 * nn, abs=1024)
     # Tall input has the same workspace as its transpose.
