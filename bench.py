@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b-mlp",
                     choices=["llama8b-mlp", "llama8b-down", "llama8b-square",
-                             "moe-experts", "moe-experts-t", "small-fp32"])
+                             "moe-experts", "moe-experts-t", "small-fp32",
+                             "copy-calibration"])
     ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
     ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
     ap.add_argument("--restart-mask", type=int, default=1 << 4)
@@ -205,8 +206,38 @@ def cpu_baseline(m_cpu, mode, restart_mask):
                       f"{dt:.1f} s"}
 
 
+def copy_calibration(args):
+    """A plain 1 GiB device-to-device copy, for scaling HBM byte counters.
+
+    rocprofv3's FETCH_SIZE and WRITE_SIZE counters of this copy read against
+    its known 1 GiB read and 1 GiB write give the factor by which the
+    counters of the product kernels are scaled.
+    """
+    import torch
+    n = 1 << 29                                   # bf16 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    print(json.dumps({"workload": "copy-calibration", "bytes_read": 2 * n,
+                      "bytes_written": 2 * n, "ms_per_copy": ms,
+                      "gbs": 4 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "copy-calibration":
+        copy_calibration(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} "
               "is not supported (multi-GPU sharding is described in the design "

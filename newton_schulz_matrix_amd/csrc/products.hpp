@@ -438,17 +438,30 @@ struct NNArgs {
   int32_t* d_status;
 };
 
-// Upper-triangle tile index -> (tm, tn), tm <= tn, row-major over the
-// upper triangle: row tm holds tiles - tm entries.
-__device__ __forceinline__ void tri_tile(int idx, int tiles, int& tm, int& tn) {
-  int r = 0;
-  int left = idx;
-  while (left >= tiles - r) {
-    left -= tiles - r;
-    ++r;
+// Work-groups are dealt to the 8 XCDs round-robin (work-group b runs on XCD
+// b % 8), and each XCD has its own L2.  xcd_order(b, count) returns the
+// position of work-group b in a list of `count` tiles cut into 8 contiguous
+// pieces, piece x for XCD x, so tiles that are neighbours in the list (and
+// share operand panels) run on the same XCD.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_order(int b, int count) {
+  const int x = b % kXcds, j = b / kXcds;
+  const int per = count / kXcds, extra = count % kXcds;  // XCD x runs per + (x < extra) work-groups
+  return x * per + (x < extra ? x : extra) + j;
+}
+
+// Upper-triangle tiles listed row pair by row pair: rows p and nt-1-p hold
+// nt - p and p + 1 tiles, nt + 1 together, so a piece of the list covers few
+// row panels (the L operand) and the column panels right of them.
+__device__ __forceinline__ void tri_tile(int idx, int nt, int& tm, int& tn) {
+  const int p = idx / (nt + 1), rem = idx % (nt + 1);
+  if (rem < nt - p) {
+    tm = p;
+    tn = p + rem;
+  } else {
+    tm = nt - 1 - p;
+    tn = tm + rem - (nt - p);
   }
-  tm = r;
-  tn = r + left;
 }
 
 // Output tile staged in LDS (the stage buffers are free after the main
@@ -496,7 +509,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
   constexpr int FM = Acc<T, TILE>::FM;
   using TL = TileLds<T, TILE>;
   int tm, tn;
-  tri_tile(blockIdx.x, p.tiles, tm, tn);
+  const int ntri = p.tiles * (p.tiles + 1) / 2;
+  tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
   const int bz = blockIdx.y;
   const int64_t ldk_bytes = (int64_t)p.ldk * sizeof(T);
   const char* Lg = reinterpret_cast<const char*>(p.L + bz * p.sL) + (int64_t)tm * TILE * ldk_bytes;

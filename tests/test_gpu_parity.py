@@ -189,6 +189,19 @@ def test_exact_symmetry_and_orientation():
 
 
 # ---------------------------------------------------------------------------
+# Larger single matrices with 256-wide tiles and ragged edges.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(2048, 4096), (2600, 2304), (1792, 5000)])
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+def test_parity_large_ragged(shape, mode):
+    m = workloads.column_scaled(shape[0], shape[1], seed=31, dtype="bf16")
+    err = _rel(_run(m, mode), _oracle(m.double().numpy(), mode))
+    print(f"{shape} {mode}: rel err {err:.3e}")
+    assert err < 1e-2
+
+
+# ---------------------------------------------------------------------------
 # Batched launcher.
 # ---------------------------------------------------------------------------
 
