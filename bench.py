@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
     ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
     ap.add_argument("--restart-mask", type=int, default=1 << 4)
+    ap.add_argument("--tile", type=int, default=0, choices=[0, 128, 192, 256],
+                    help="force the products' tile edge (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-form companion measurement")
@@ -142,10 +144,11 @@ def run_form(x, mode, steps, warmup, args, trace_kinds=None):
     rows, cols = x.shape[-2], x.shape[-1]
     ws = torch.empty(nsa.workspace_size(rows, cols, x.shape[0] if batched
                                         else 1, x.dtype, mode,
-                                        args.restart_mask, args.internal)
+                                        args.restart_mask, args.internal,
+                                        args.tile)
                      + 256, dtype=torch.uint8, device=x.device)
     kw = dict(mode=mode, restart_mask=args.restart_mask,
-              internal=args.internal, workspace=ws)
+              internal=args.internal, workspace=ws, tile=args.tile)
     # One untraced call first: the first launch of each kernel also loads
     # its code object.  Then warm-up calls with every kind traced, to find
     # the dominant kernel.
@@ -306,6 +309,7 @@ def main():
                    "batch": batch, "io_dtype": io, "mode": args.mode,
                    "ns_steps": 5, "abc": list(nsa.TUNED_ABC),
                    "restart_mask": args.restart_mask,
+                   "tile": args.tile or "auto",
                    "parallelism": "single-gpu"},
         "tflops": tflops,
         "mfma_frac": tflops / PEAK_TFLOPS[dtype],

@@ -105,6 +105,11 @@ typedef struct ns_options {
   int32_t* d_status;
   /* Optional launch trace (see ns_trace); NULL for none. */
   ns_trace* trace;
+  /* Tile edge of the matrix products: 0 = automatic (a cost estimate for
+   * MI355X picks it from the shape and batch), or 128, 192 or 256 (192 and
+   * 256 for 16-bit products only).  Results do not depend on it beyond
+   * fp32 accumulation order; it changes the workspace size. */
+  int32_t tile;
 } ns_options;
 
 /* Fill *opt with the defaults above. */

@@ -57,7 +57,8 @@ class Options(ctypes.Structure):
                 ("eps", ctypes.c_float),
                 ("internal", ctypes.c_int32),
                 ("d_status", ctypes.c_void_p),
-                ("trace", ctypes.POINTER(Trace))]
+                ("trace", ctypes.POINTER(Trace)),
+                ("tile", ctypes.c_int32)]
 
 
 KERNEL_KINDS = ("norm", "stage", "gram", "sym", "update", "threshold")
@@ -153,9 +154,10 @@ def dtype_code(dtype: torch.dtype) -> int:
 def make_options(restart_mask: int = 1 << 4, eps: float = 1e-7,
                  internal: Optional[str] = None,
                  status: Optional[torch.Tensor] = None,
-                 trace: Optional[Trace] = None) -> Options:
+                 trace: Optional[Trace] = None, tile: int = 0) -> Options:
     opt = Options()
     lib().ns_options_default(ctypes.byref(opt))
+    opt.tile = int(tile)
     opt.restart_mask = int(restart_mask)
     opt.eps = float(eps)
     opt.internal = _INTERNAL_CODE[internal]
@@ -196,8 +198,8 @@ def _workspace(nbytes: int, device: torch.device,
 def workspace_size(rows: int, cols: int, batch: int = 1,
                    dtype: torch.dtype = torch.bfloat16,
                    mode: str = "standard", restart_mask: int = 1 << 4,
-                   internal: Optional[str] = None) -> int:
-    opt = make_options(restart_mask, 1e-7, internal)
+                   internal: Optional[str] = None, tile: int = 0) -> int:
+    opt = make_options(restart_mask, 1e-7, internal, tile=tile)
     return int(lib().ns_workspace_size(rows, cols, batch, dtype_code(dtype),
                                        _MODE_CODE[mode], ctypes.byref(opt)))
 
@@ -216,13 +218,16 @@ def orthogonalize(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
                   eps: float = 1e-7, internal: Optional[str] = None,
                   status: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None,
-                  trace: Optional[Trace] = None) -> torch.Tensor:
-    """Orthogonalize a 2-D device matrix in place; returns it."""
+                  trace: Optional[Trace] = None, tile: int = 0) -> torch.Tensor:
+    """Orthogonalize a 2-D device matrix in place; returns it.
+
+    ``tile`` forces the products' tile edge (128, 192 or 256; 0 = automatic).
+    """
     _check_matrix(x, 2)
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
     code = dtype_code(x.dtype)
-    opt = make_options(restart_mask, eps, internal, status, trace)
+    opt = make_options(restart_mask, eps, internal, status, trace, tile)
     need = int(lib().ns_workspace_size(rows, cols, 1, code, _MODE_CODE[mode],
                                        ctypes.byref(opt)))
     if need == 0:
@@ -242,14 +247,15 @@ def orthogonalize_batched(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
                           eps: float = 1e-7, internal: Optional[str] = None,
                           status: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None,
-                          trace: Optional[Trace] = None) -> torch.Tensor:
+                          trace: Optional[Trace] = None,
+                          tile: int = 0) -> torch.Tensor:
     """Orthogonalize each x[e] of a [E, rows, cols] device tensor in place."""
     _check_matrix(x, 3)
     batch, rows, cols = x.shape
     ld = x.stride(1) if rows > 1 else cols
     bstride = x.stride(0) if batch > 1 else rows * ld
     code = dtype_code(x.dtype)
-    opt = make_options(restart_mask, eps, internal, status, trace)
+    opt = make_options(restart_mask, eps, internal, status, trace, tile)
     need = int(lib().ns_workspace_size(rows, cols, batch, code,
                                        _MODE_CODE[mode], ctypes.byref(opt)))
     if need == 0:

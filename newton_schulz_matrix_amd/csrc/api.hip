@@ -31,15 +31,21 @@ struct Plan {
   int64_t rows = 0, cols = 0, n = 0, m = 0, n_pad = 0, m_pad = 0;
   int64_t batch = 1;
   bool transposed = false;
-  int tile = 256;
+  int tile = 256;    // edge of the square tiles of the symmetric products (rows of nn tiles)
+  int tile_n = 256;  // columns of nn tiles
   ns_dtype io = NS_BF16, internal = NS_FP16;
   ns_mode mode = NS_STANDARD;
   int esz = 2;
   int partials = 1;
   int nn_count = 2;
   int64_t x_elems = 0, nn_elems = 0;
-  size_t off_partial = 0, off_scale = 0, off_x[2] = {0, 0}, off_nn[4] = {0, 0, 0, 0}, total = 0;
+  size_t off_partial = 0, off_scale = 0, off_x[2] = {0, 0}, off_xt[2] = {0, 0}, off_nn[4] = {0, 0, 0, 0};
+  size_t total = 0;
 };
+
+// Columns of the update tiles that go with a square tile edge: square tiles
+// where three pipeline stages fit in LDS (128, 192), 256 otherwise.
+constexpr int nn_tile_n(int edge) { return edge; }
 
 bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
   const int req = opt ? opt->internal : -1;
@@ -60,12 +66,50 @@ bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
   return false;
 }
 
-// Tile edge: 256 when the small side is large and needs no extra padding
-// for it (16-bit products only), else 128.
-int pick_tile(int64_t n, ns_dtype internal) {
-  if (internal == NS_FP32) return 128;  // an fp32 256 x 256 tile does not fit in LDS
-  if (n >= 512 && round_up(n, 256) == round_up(n, 128)) return 256;
-  return 128;
+// Tile edge.  fp32 products use 128 (a larger fp32 tile does not fit in
+// LDS).  For 16-bit products the edge (128, 192 or 256) minimizes a cost
+// estimate of one call: work-group waves over the 256 compute units times
+// the time of one work-group, in units of one 256-edge k-tile, with the
+// per-k-tile and fixed (prologue and epilogue) costs measured on MI355X.
+// Smaller tiles lose MFMA efficiency (more LDS reads per MFMA) but fill the
+// chip when a product has few tiles.
+struct TileCost {
+  int edge;
+  double sym_ktile, sym_fixed, nn_ktile, nn_fixed;
+};
+constexpr TileCost kTileCosts[] = {
+    {128, 0.40, 8.0, 0.40, 8.0},
+    {192, 0.55, 13.5, 0.55, 15.0},
+    {256, 1.00, 22.0, 1.00, 24.0},
+};
+constexpr double kComputeUnits = 256.0;
+
+double tile_estimate(const TileCost& c, int64_t n, int64_t m, int64_t batch, ns_mode mode) {
+  const int64_t n_pad = round_up(n, c.edge), tn = nn_tile_n(c.edge), m_pad = round_up(m, tn);
+  const double nt = (double)(n_pad / c.edge);
+  const double sym_waves = ceil(nt * (nt + 1) / 2 * (double)batch / kComputeUnits);
+  const double nn_waves = ceil(nt * (double)(m_pad / tn) * (double)batch / kComputeUnits);
+  const double kn = (double)n_pad / 64, km = (double)m_pad / 64;
+  const double sym = sym_waves * (kn * c.sym_ktile + c.sym_fixed);
+  const double gram = sym_waves * (km * c.sym_ktile + c.sym_fixed);
+  const double nn = nn_waves * (kn * c.nn_ktile + c.nn_fixed);
+  // Launch counts of five steps: standard 5 X X^T, 5 n x n, 5 updates; Gram
+  // (one restart) 2 X X^T, about 14 n x n products and 2 updates.
+  return mode == NS_GRAM ? 2 * gram + 14 * sym + 2 * nn : 5 * (gram + sym + nn);
+}
+
+int pick_tile(int64_t n, int64_t m, int64_t batch, ns_dtype internal, ns_mode mode) {
+  if (internal == NS_FP32) return 128;
+  int best = 128;
+  double best_t = 0.0;
+  for (const TileCost& c : kTileCosts) {
+    const double t = tile_estimate(c, n, m, batch, mode);
+    if (c.edge == 128 || t < best_t) {
+      best = c.edge;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_mode mode, const ns_options* opt,
@@ -84,9 +128,13 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
   p->transposed = rows > cols;
   p->n = p->transposed ? cols : rows;
   p->m = p->transposed ? rows : cols;
-  p->tile = pick_tile(p->n, internal);
+  const int req_tile = opt ? opt->tile : 0;
+  if (req_tile != 0 && !(req_tile == 128 || (internal != NS_FP32 && (req_tile == 192 || req_tile == 256))))
+    return NS_ERR_INVALID_ARG;
+  p->tile = req_tile ? req_tile : pick_tile(p->n, p->m, batch, internal, mode);
+  p->tile_n = nn_tile_n(p->tile);
   p->n_pad = round_up(p->n, p->tile);
-  p->m_pad = round_up(p->m, p->tile);
+  p->m_pad = round_up(p->m, p->tile_n);
   p->esz = elem_size(internal);
   p->x_elems = p->n_pad * p->m_pad;
   p->nn_elems = p->n_pad * p->n_pad;
@@ -103,6 +151,8 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
   off = align_up(off + (size_t)batch * sizeof(float));
   for (int i = 0; i < 2; ++i) {
     p->off_x[i] = off;
+    off = align_up(off + (size_t)batch * p->x_elems * p->esz);
+    p->off_xt[i] = off;
     off = align_up(off + (size_t)batch * p->x_elems * p->esz);
   }
   for (int i = 0; i < p->nn_count; ++i) {
@@ -149,9 +199,9 @@ hipError_t launch_sym(const SymArgs<T>& a, int64_t batch, hipStream_t s) {
 }
 
 template <typename T, typename OutT, int TILE>
-hipError_t launch_nn(const NNArgs<T, OutT>& a, int64_t batch, hipStream_t s) {
+hipError_t launch_nt(const NTArgs<T, OutT>& a, int64_t batch, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n, (unsigned)batch);
-  hipLaunchKernelGGL((k_nn<T, OutT, TILE>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE)>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -167,6 +217,7 @@ struct Runner {
   Tracer tr;
 
   T* xbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_x[i]); }
+  T* xtbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_xt[i]); }
   T* nnbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_nn[i]); }
 
   // C = beta*E + gamma * L R^T on upper tiles, mirrored.  L and R are the
@@ -208,23 +259,29 @@ struct Runner {
     return tr.run(NS_KERNEL_SYM, flops, bytes, [&] { return launch_sym<T, TILE, false>(a, p.batch, st); });
   }
 
+  // Y = alpha * X_in + B X_in into X_out and X_out^T (E omitted when alpha
+  // is 0).
   template <int TILE>
-  hipError_t nn_internal(const T* B, const T* X, const T* E, float alpha, T* Y) const {
-    NNArgs<T, T> a;
+  hipError_t nn_internal(const T* B, int xin, bool with_e, float alpha, int xout) const {
+    NTArgs<T, T> a;
     a.B = B;
-    a.X = X;
-    a.E = E;
-    a.Y = Y;
+    a.XT = xtbuf(xin);
+    a.E = with_e ? xbuf(xin) : nullptr;
+    a.Y = xbuf(xout);
+    a.YT = xtbuf(xout);
     a.sB = p.nn_elems;
-    a.sX = p.x_elems;
+    a.sXT = p.x_elems;
     a.sE = p.x_elems;
     a.sY = p.x_elems;
+    a.sYT = p.x_elems;
     a.ldb = (int)p.n_pad;
-    a.ldx = (int)p.m_pad;
+    a.ldxt = (int)p.n_pad;
+    a.lde = (int)p.m_pad;
+    a.ldyt = (int)p.n_pad;
     a.ldy = p.m_pad;
     a.K = (int)p.n_pad;
     a.tiles_m = (int)(p.n_pad / TILE);
-    a.tiles_n = (int)(p.m_pad / TILE);
+    a.tiles_n = (int)(p.m_pad / nn_tile_n(TILE));
     a.n_real = (int)p.n;
     a.m_real = (int)p.m;
     a.transpose_out = 0;
@@ -234,28 +291,33 @@ struct Runner {
     a.out_scale = 1.f;
     a.d_status = nullptr;
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
-    const double bytes = bt * (n * n * es + n * m * es * (2.0 + (E ? 1.0 : 0.0)));
+    const double bytes = bt * (n * n * es + n * m * es * (3.0 + (with_e ? 1.0 : 0.0)));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
-                  [&] { return launch_nn<T, T, TILE>(a, p.batch, st); });
+                  [&] { return launch_nt<T, T, TILE>(a, p.batch, st); });
   }
 
+  // The caller's matrix = out_scale * (alpha * X_in + B X_in), oriented back.
   template <int TILE>
-  hipError_t nn_final(const T* B, const T* X, const T* E, float alpha, float out_scale) const {
-    NNArgs<T, IO> a;
+  hipError_t nn_final(const T* B, int xin, bool with_e, float alpha, float out_scale) const {
+    NTArgs<T, IO> a;
     a.B = B;
-    a.X = X;
-    a.E = E;
+    a.XT = xtbuf(xin);
+    a.E = with_e ? xbuf(xin) : nullptr;
     a.Y = user;
+    a.YT = nullptr;
     a.sB = p.nn_elems;
-    a.sX = p.x_elems;
+    a.sXT = p.x_elems;
     a.sE = p.x_elems;
     a.sY = bstride;
+    a.sYT = 0;
     a.ldb = (int)p.n_pad;
-    a.ldx = (int)p.m_pad;
+    a.ldxt = (int)p.n_pad;
+    a.lde = (int)p.m_pad;
+    a.ldyt = 0;
     a.ldy = ld;
     a.K = (int)p.n_pad;
     a.tiles_m = (int)(p.n_pad / TILE);
-    a.tiles_n = (int)(p.m_pad / TILE);
+    a.tiles_n = (int)(p.m_pad / nn_tile_n(TILE));
     a.n_real = (int)p.n;
     a.m_real = (int)p.m;
     a.transpose_out = p.transposed ? 1 : 0;
@@ -265,9 +327,9 @@ struct Runner {
     a.out_scale = out_scale;
     a.d_status = opt ? opt->d_status : nullptr;
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
-    const double bytes = bt * (n * n * es + n * m * es * (1.0 + (E ? 1.0 : 0.0)) + n * m * sizeof(IO));
+    const double bytes = bt * (n * n * es + n * m * es * (1.0 + (with_e ? 1.0 : 0.0)) + n * m * sizeof(IO));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
-                  [&] { return launch_nn<T, IO, TILE>(a, p.batch, st); });
+                  [&] { return launch_nt<T, IO, TILE>(a, p.batch, st); });
   }
 
   hipError_t stage(float prescale, float eps) const {
@@ -286,17 +348,11 @@ struct Runner {
     hipLaunchKernelGGL(k_scale, dim3((unsigned)p.batch), dim3(kStageThreads), 0, st, partial, p.partials, prescale,
                        eps, scales);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return tr.run(NS_KERNEL_STAGE, 0.0, elems * (sizeof(IO) + sizeof(T)), [&] {
-      if (!p.transposed) {
-        hipLaunchKernelGGL((k_stage_rows<IO, T>), dim3((unsigned)p.n_pad, (unsigned)p.batch), dim3(kStageThreads),
-                           0, st, user, p.rows, p.cols, ld, bstride, scales, xbuf(0), p.m_pad, p.x_elems);
-      } else {
-        const int tj = (int)(p.m_pad / 64);
-        const int ti = (int)(p.n_pad / 64);
-        hipLaunchKernelGGL((k_stage_transpose<IO, T>), dim3((unsigned)(ti * tj), (unsigned)p.batch),
-                           dim3(kStageThreads), 0, st, user, p.rows, p.cols, ld, bstride, scales, xbuf(0), p.m_pad,
-                           p.x_elems, tj);
-      }
+    return tr.run(NS_KERNEL_STAGE, 0.0, elems * (sizeof(IO) + 2 * sizeof(T)), [&] {
+      const int bi = (int)(p.n_pad / 64), bj = (int)(p.m_pad / 64);
+      hipLaunchKernelGGL((k_stage_pair<IO, T>), dim3((unsigned)(bi * bj), (unsigned)p.batch), dim3(kStageThreads),
+                         0, st, user, p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, scales, xbuf(0), xtbuf(0),
+                         p.n_pad, p.m_pad, p.x_elems, p.transposed ? 1 : 0, bj);
       return hipGetLastError();
     });
   }
@@ -319,10 +375,10 @@ struct Runner {
         if ((e = sym<TILE>(X, X, mp, mp, nullptr, 0.f, gram_scale, A, nullptr, 0.f)) != hipSuccess) return e;
         if ((e = sym<TILE>(A, A, np, np, A, b[k], c[k], B, nullptr, 0.f)) != hipSuccess) return e;
         if (k + 1 < steps) {
-          if ((e = nn_internal<TILE>(B, X, X, a[k], xbuf(xi ^ 1))) != hipSuccess) return e;
+          if ((e = nn_internal<TILE>(B, xi, true, a[k], xi ^ 1)) != hipSuccess) return e;
           xi ^= 1;
         } else {
-          if ((e = nn_final<TILE>(B, X, X, a[k], unscale)) != hipSuccess) return e;
+          if ((e = nn_final<TILE>(B, xi, true, a[k], unscale)) != hipSuccess) return e;
         }
       }
       return hipSuccess;
@@ -337,7 +393,7 @@ struct Runner {
     bool fresh = true;
     for (int k = 1; k <= steps; ++k) {
       if (k > 1 && ((mask >> k) & 1u)) {
-        if ((e = nn_internal<TILE>(Qb[qi], xbuf(xi), nullptr, 0.f, xbuf(xi ^ 1))) != hipSuccess) return e;
+        if ((e = nn_internal<TILE>(Qb[qi], xi, false, 0.f, xi ^ 1)) != hipSuccess) return e;
         xi ^= 1;
         if ((e = sym<TILE>(xbuf(xi), xbuf(xi), mp, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f)) != hipSuccess)
           return e;
@@ -359,7 +415,7 @@ struct Runner {
         if ((e = sym<TILE>(Z, V, np, np, V, ak, 1.f, R, nullptr, 0.f)) != hipSuccess) return e;
       }
     }
-    return nn_final<TILE>(Qb[qi], xbuf(xi), nullptr, 0.f, unscale);
+    return nn_final<TILE>(Qb[qi], xi, false, 0.f, unscale);
   }
 };
 
@@ -373,7 +429,11 @@ ns_status run_typed(const Plan& p, void* X, int64_t ld, int64_t bstride, int ste
   if constexpr (sizeof(T) == 4) {
     e = r.template run<128>(steps, a, b, c, eps);
   } else {
-    e = (p.tile == 256) ? r.template run<256>(steps, a, b, c, eps) : r.template run<128>(steps, a, b, c, eps);
+    switch (p.tile) {
+      case 256: e = r.template run<256>(steps, a, b, c, eps); break;
+      case 192: e = r.template run<192>(steps, a, b, c, eps); break;
+      default: e = r.template run<128>(steps, a, b, c, eps); break;
+    }
   }
   return hip_status(e);
 }
@@ -474,6 +534,7 @@ void ns_options_default(ns_options* opt) {
   opt->internal = -1;
   opt->d_status = nullptr;
   opt->trace = nullptr;
+  opt->tile = 0;
 }
 
 size_t ns_workspace_size(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode,

@@ -1,31 +1,36 @@
 // products.hpp - MFMA tile engine for the matrix products of Newton-Schulz.
 //
-// Every product in both Newton-Schulz forms is one of two shapes:
+// Every product in both Newton-Schulz forms is one of two shapes, both of
+// the form L R^T with L and R stored row-major with K contiguous:
 //
-//   sym  : C = beta*E + gamma * L R^T   (L, R: n x K row-major, C, E: n x n)
+//   sym  : C = beta*E + gamma * L R^T   (L, R: n x K, C, E: n x n)
 //          with a symmetric result, so only tiles (tm <= tn) are computed and
 //          each is also stored mirrored.  X X^T, A A (A symmetric), Z' Q,
 //          Z' R and Z' V are all of this shape (Q, R, V, Z' are polynomials
 //          in the same Gram matrix, so they are symmetric and commute).
-//   nn   : C = alpha*E + gamma * B X   (B: n x n, X: n x m row-major)
-//          the update X <- a X + B X and the Gram form's Q X.
+//   nt   : Y = alpha*E + gamma * B X = alpha*E + gamma * B (X^T)^T
+//          (B: n x n, X^T: m x n), the update X <- a X + B X and the Gram
+//          form's Q X.  X is kept in both layouts, X (n x m, for X X^T and
+//          the a X term) and X^T (m x n, for this product), and an update
+//          whose result feeds another update writes both.
 //
 // Tile engine (gfx950, CDNA4):
-//   * 256 threads = 4 wave64s in a 2 x 2 grid; block tile TILE x TILE
-//     (TILE = 256 or 128); each wave owns a (TILE/2)^2 sub-tile made of
-//     32 x 32 MFMA tiles (v_mfma_f32_32x32x16_{f16,bf16}; for fp32 operands
-//     four v_mfma_f32_32x32x2_f32 per 16-byte chunk).
+//   * 256 threads = 4 wave64s in a 2 x 2 grid; block tile TM x TN (sym:
+//     square, 128, 192 or 256; nn: 128 x 128, 192 x 256 or 256 x 256); each
+//     wave owns a (TM/2) x (TN/2) sub-tile made of 32 x 32 MFMA tiles
+//     (v_mfma_f32_32x32x16_{f16,bf16}; for fp32 operands four
+//     v_mfma_f32_32x32x2_f32 per 16-byte chunk).  The 192 edge exists for
+//     occupancy: a 4096 x 4096 symmetric product has 136 upper-triangle
+//     tiles of 256 but 253 of 192, for 256 compute units.
 //   * K is consumed in k-tiles of 128 bytes per operand row (64 16-bit or
-//     32 fp32 elements), staged through LDS with two buffers; global loads
-//     of k-tile t+1 are in flight while k-tile t feeds the MFMAs.
+//     32 fp32 elements), staged through LDS with two buffers; the copies of
+//     k-tile t+2 are in flight while k-tiles t and t+1 feed the MFMAs.
 //   * LDS rows are 128 bytes made of eight 16-byte chunks; chunk c of row r
 //     lives at slot c ^ ((r ^ (r >> 3)) & 7), so the 32 rows an MFMA operand
 //     read touches, and the transposed writes of the nn loader, spread over
 //     the banks.
-//   * Both operands are read from LDS the same way (row r, 8 consecutive k),
-//     so a K-contiguous operand is copied straight through, and the X
-//     operand of nn (k is its row index) is transposed in registers on its
-//     way from global memory to LDS (8 x 8 blocks of 16-bit elements).
+//   * Both operands are read from LDS the same way (row r, 8 consecutive k)
+//     and copied straight from global memory into LDS.
 //   * The MFMA's first operand is the right-hand matrix, so each lane ends
 //     up holding four consecutive columns of one output row, which makes the
 //     fp32 epilogue (alpha*E + gamma*acc, casts) work on 8- or 16-byte
@@ -120,15 +125,16 @@ template <> __device__ __forceinline__ void mma_chunk<float>(const uint4& a, con
 // Global -> LDS loaders.
 // ---------------------------------------------------------------------------
 
-// K-contiguous operand: TILE rows of 128 bytes per k-tile, copied straight
+// K-contiguous operand: ROWS rows of 128 bytes per k-tile, copied straight
 // from global memory into LDS (global_load_lds_dwordx4: lane L of a wave
 // writes its 16 bytes at M0 + 16 L).  One instruction fills 8 LDS rows; lane
 // L fetches the chunk that belongs at slot L & 7 of row L >> 3, so the LDS
 // swizzle is applied on the global side.  Row r = 8 q + (L >> 3) of the wave
 // has swz(r) = (L >> 3) ^ (q & 7).
-template <int TILE>
+template <int ROWS>
 struct DmaLoader {
-  static constexpr int kRowsPerWave = TILE / 4;
+  static_assert(ROWS % 32 == 0, "each wave fills whole groups of 8 rows");
+  static constexpr int kRowsPerWave = ROWS / 4;
   static constexpr int kIters = kRowsPerWave / 8;
   uint32_t lane_off;   // (L >> 3) * ld + 16 * ((L & 7) ^ (L >> 3))
   uint32_t ld8;        // 8 * ld (bytes), uniform
@@ -155,250 +161,283 @@ struct DmaLoader {
   }
 };
 
-// X operand of nn: k runs along X's rows.  A k-tile is BK rows x TILE
-// columns of X; it is stored in LDS as TILE rows (one per column of X) of
-// BK k-values, by transposing E x E blocks in registers.  Thread t owns
-// column block jb = t % JB and k block kb = t / JB.
-template <typename T, int TILE>
-struct ColLoader {
-  static constexpr int E = 16 / sizeof(T);        // elements per chunk
-  static constexpr int BK = 8 * E;                // k values per k-tile
-  static constexpr int JB = TILE / E;             // column blocks
-  static constexpr int NBLK = (BK / E) * JB;
-  static constexpr int kPer = (NBLK + kThreads - 1) / kThreads;
-  uint4 r[kPer][E];
-  __device__ __forceinline__ void load(const char* g, int64_t ld_bytes, int kt) {
-    const char* gk = g + (int64_t)kt * BK * ld_bytes;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int b = threadIdx.x + i * kThreads;
-      if (NBLK % kThreads == 0 || b < NBLK) {
-        const int jb = b % JB, kb = b / JB;
-        const uint32_t off = (uint32_t)(kb * E * ld_bytes) + (uint32_t)(jb * 16);
-#pragma unroll
-        for (int rr = 0; rr < E; ++rr)
-          r[i][rr] = *reinterpret_cast<const uint4*>(gk + (off + (uint32_t)(rr * ld_bytes)));
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* s) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int b = threadIdx.x + i * kThreads;
-      if (NBLK % kThreads == 0 || b < NBLK) {
-        const int jb = b % JB, kb = b / JB;
-        // Row j = jb*E + jj; for E == 8, swz(j) = jj ^ (jb & 7).
-        const uint32_t* in = reinterpret_cast<const uint32_t*>(&r[i][0]);
-        if constexpr (E == 8) {
-          // 8 x 8 block of 16-bit values: in[rr].dword[d] = (col 2d, col 2d+1)
-          // of k-row rr; out[jj].dword[e] = (k 2e, k 2e+1) of column jj.
-          char* base = s + jb * 8 * kRowBytes;
-          const int x = kb ^ (jb & 7);
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t lo = in[(2 * e) * 4 + (jj >> 1)];
-              const uint32_t hi = in[(2 * e + 1) * 4 + (jj >> 1)];
-              o[e] = (jj & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-            *reinterpret_cast<uint4*>(base + jj * kRowBytes + ((x ^ jj) << 4)) = uint4{o[0], o[1], o[2], o[3]};
-          }
-        } else {
-          // 4 x 4 block of fp32 values.
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            *reinterpret_cast<uint4*>(s + lds_off(jb * 4 + jj, kb)) =
-                uint4{in[0 * 4 + jj], in[1 * 4 + jj], in[2 * 4 + jj], in[3 * 4 + jj]};
-          }
-        }
-      }
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // Main loop: acc[fm][fn] += L-tile * R-tile^T over a range of k-tiles.
 // ---------------------------------------------------------------------------
-template <int FM>
+// Fragments of one substep: FN 32-row pieces of R, FM of L.
+template <int FM, int FN>
 struct Frags {
-  uint4 a[FM], b[FM];
+  uint4 a[FN], b[FM];
 };
 
 // Per-lane LDS byte offsets of this wave's fragment rows.  Fragment i of a
-// wave covers rows w0 + 32 i + (L & 31) with w0 a multiple of 64, so
-// swz(row) = (L & 7) ^ (4 (i & 1) + ((L & 31) >> 3)) only depends on the
-// parity of i; the offset of (i, chunk c) is row0 + 4096 i + 16 (c ^ swz).
+// wave covers rows w0 + 32 i + (L & 31) with w0 a multiple of 32, so
+// swz(row) = (L & 7) ^ (((w0 >> 3) + 4 i + ((L & 31) >> 3)) & 7) only
+// depends on the parity of i; the offset of (i, chunk c) is
+// row0 + 4096 i + 16 (c ^ swz).
 struct FragAddr {
   uint32_t row0L, row0R;  // (w0 + (L & 31)) * 128 for the L and R operands
-  int sw0, sw1;           // swz for even and odd i
+  int swL0, swL1, swR0, swR1;  // swz for even and odd i
   __device__ __forceinline__ void init(int wr, int wc) {
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 31;
+    const int lr = threadIdx.x & 31;
     row0L = (uint32_t)((wr + lr) * kRowBytes);
     row0R = (uint32_t)((wc + lr) * kRowBytes);
-    sw0 = (lr & 7) ^ (lr >> 3);
-    sw1 = (lr & 7) ^ (4 + (lr >> 3));
+    swL0 = swz(wr + lr);
+    swL1 = swz(wr + 32 + lr);
+    swR0 = swz(wc + lr);
+    swR1 = swz(wc + 32 + lr);
   }
 };
 
 // Fragments of substep s (16-byte chunk pair 2s, 2s+1) for this wave.
-template <int FM>
+template <int FM, int FN>
 __device__ __forceinline__ void load_frags(const char* sL, const char* sR, const FragAddr& fa, int s,
-                                           Frags<FM>& f) {
-  const int h = (threadIdx.x & 63) >> 5;
-  const uint32_t c0 = (uint32_t)(((2 * s + h) ^ fa.sw0) << 4);
-  const uint32_t c1 = (uint32_t)(((2 * s + h) ^ fa.sw1) << 4);
+                                           Frags<FM, FN>& f) {
+  const int c = 2 * s + ((threadIdx.x & 63) >> 5);
+  const uint32_t r0 = (uint32_t)((c ^ fa.swR0) << 4), r1 = (uint32_t)((c ^ fa.swR1) << 4);
+  const uint32_t l0 = (uint32_t)((c ^ fa.swL0) << 4), l1 = (uint32_t)((c ^ fa.swL1) << 4);
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+    f.a[i] = *reinterpret_cast<const uint4*>(sR + (fa.row0R + ((i & 1) ? r1 : r0)) + i * 32 * kRowBytes);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
-    f.a[i] = *reinterpret_cast<const uint4*>(sR + (fa.row0R + ((i & 1) ? c1 : c0)) + i * 32 * kRowBytes);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-    f.b[i] = *reinterpret_cast<const uint4*>(sL + (fa.row0L + ((i & 1) ? c1 : c0)) + i * 32 * kRowBytes);
+    f.b[i] = *reinterpret_cast<const uint4*>(sL + (fa.row0L + ((i & 1) ? l1 : l0)) + i * 32 * kRowBytes);
 }
 
-template <typename T, int FM>
-__device__ __forceinline__ void mma_frags(const Frags<FM>& f, f32x16 (&acc)[FM][FM]) {
+template <typename T, int FM, int FN>
+__device__ __forceinline__ void mma_frags(const Frags<FM, FN>& f, f32x16 (&acc)[FM][FN]) {
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < FM; ++fn) mma_chunk<T>(f.a[fn], f.b[fm], acc[fm][fn]);
+    for (int fn = 0; fn < FN; ++fn) mma_chunk<T>(f.a[fn], f.b[fm], acc[fm][fn]);
 }
 
-// All four substeps of one k-tile, with the fragments of substep s+1 read
-// from LDS while the MFMAs of substep s run.  `mid` runs between substeps 1
-// and 2 (the nn kernel stores its transposed operand there).
-template <typename T, int TILE, class Mid>
-__device__ __forceinline__ void compute_ktile(const char* sL, const char* sR, const FragAddr& fa,
-                                              f32x16 (&acc)[TILE / 64][TILE / 64], Mid&& mid) {
-  constexpr int FM = TILE / 64;
-  Frags<FM> f0, f1;
-  load_frags<FM>(sL, sR, fa, 0, f0);
-  load_frags<FM>(sL, sR, fa, 1, f1);
-  mma_frags<T, FM>(f0, acc);
-  load_frags<FM>(sL, sR, fa, 2, f0);
-  mma_frags<T, FM>(f1, acc);
-  mid();
-  load_frags<FM>(sL, sR, fa, 3, f1);
-  mma_frags<T, FM>(f0, acc);
-  mma_frags<T, FM>(f1, acc);
-}
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8); a field at its maximum does not wait.
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
 
-// Instruction order for a k-tile of the DMA path (one basic block): the
-// global->LDS copies of the next k-tile first, the fragment reads of
-// substeps 0 and 1, then the reads of substeps 2 and 3 spread between the
-// MFMAs of substeps 0 and 1, then the MFMAs of substeps 2 and 3.  The MFMA
-// count per 16-byte chunk is 1 (16-bit) or 4 (fp32).
-template <typename T, int TILE>
-__device__ __forceinline__ void schedule_dma_ktile() {
-  constexpr int FM = TILE / 64;
-  constexpr int NR = 2 * FM;                                   // reads per substep
-  constexpr int NM = FM * FM * (sizeof(T) == 4 ? 4 : 1);       // MFMAs per substep
-  __builtin_amdgcn_sched_group_barrier(0x020, 2 * (TILE / 32), 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);
-}
-
-template <typename T, int TILE>
+template <typename T, int TM, int TN>
 struct Acc {
-  static constexpr int FM = TILE / 64;  // 32x32 MFMA tiles per wave per dim
-  f32x16 v[FM][FM];
+  static constexpr int FM = TM / 64;  // 32x32 MFMA tiles per wave, rows
+  static constexpr int FN = TN / 64;  // and columns
+  f32x16 v[FM][FN];
 };
 
-// The two LDS stages are distinct __shared__ objects (per tile size), so the
-// compiler can tell the DMA writes into one stage from the fragment reads of
-// the other and does not wait for the loads in flight before every read.
-// Each stage holds the L operand (TILE rows x 128 bytes) followed by the R
-// operand.
-__shared__ __attribute__((aligned(1024))) char g_stage0_256[2 * 256 * kRowBytes];
-__shared__ __attribute__((aligned(1024))) char g_stage1_256[2 * 256 * kRowBytes];
-__shared__ __attribute__((aligned(1024))) char g_stage0_128[2 * 128 * kRowBytes];
-__shared__ __attribute__((aligned(1024))) char g_stage1_128[2 * 128 * kRowBytes];
+// LDS stages are distinct __shared__ objects, so the compiler can tell the
+// DMA writes into one stage from the fragment reads of another and does not
+// wait for the copies in flight before every read.  A stage holds the L
+// operand (TM rows x 128 bytes) followed by the R operand (TN rows).  Three
+// families: 64 KiB stages (two; tiles of 256 + 256 or 192 + 256 rows), 48 KiB
+// (three; 192 + 192) and 32 KiB (three; 128 + 128).  Three stages, where
+// they fit in LDS, give every copy two pipeline steps to land.
+__shared__ __attribute__((aligned(1024))) char g_stage0_big[65536];
+__shared__ __attribute__((aligned(1024))) char g_stage1_big[65536];
+__shared__ __attribute__((aligned(1024))) char g_stage0_mid[49152];
+__shared__ __attribute__((aligned(1024))) char g_stage1_mid[49152];
+__shared__ __attribute__((aligned(1024))) char g_stage2_mid[49152];
+__shared__ __attribute__((aligned(1024))) char g_stage0_small[32768];
+__shared__ __attribute__((aligned(1024))) char g_stage1_small[32768];
+__shared__ __attribute__((aligned(1024))) char g_stage2_small[32768];
 
-template <int TILE> struct Stages;
-template <> struct Stages<256> {
-  static __device__ __forceinline__ char* s0() { return g_stage0_256; }
-  static __device__ __forceinline__ char* s1() { return g_stage1_256; }
+template <int BYTES> struct StageMem;
+template <> struct StageMem<65536> {
+  static __device__ __forceinline__ char* s0() { return g_stage0_big; }
+  static __device__ __forceinline__ char* s1() { return g_stage1_big; }
+  static __device__ __forceinline__ char* s2() { return nullptr; }
 };
-template <> struct Stages<128> {
-  static __device__ __forceinline__ char* s0() { return g_stage0_128; }
-  static __device__ __forceinline__ char* s1() { return g_stage1_128; }
+template <> struct StageMem<49152> {
+  static __device__ __forceinline__ char* s0() { return g_stage0_mid; }
+  static __device__ __forceinline__ char* s1() { return g_stage1_mid; }
+  static __device__ __forceinline__ char* s2() { return g_stage2_mid; }
+};
+template <> struct StageMem<32768> {
+  static __device__ __forceinline__ char* s0() { return g_stage0_small; }
+  static __device__ __forceinline__ char* s1() { return g_stage1_small; }
+  static __device__ __forceinline__ char* s2() { return g_stage2_small; }
 };
 
-// One k-tile: start the loads of k-tile kt+1 into `nxt` (when there is one),
-// run the MFMAs on `cur`, then wait for the loads and synchronize.
-template <typename T, int TILE, bool COL_RIGHT>
-__device__ __forceinline__ void ktile_step(const char* Lg, const char* Rg, int64_t ldr_bytes,
-                                           const DmaLoader<TILE>& la, const DmaLoader<TILE>& lb, int kt,
-                                           bool more, const char* __restrict__ cur, char* __restrict__ nxt,
-                                           const FragAddr& fa,
-                                           f32x16 (&acc)[TILE / 64][TILE / 64]) {
-  constexpr int kOpBytes = TILE * kRowBytes;
-  if constexpr (COL_RIGHT) {
-    ColLoader<T, TILE> cb;
-    if (more) {
-      la.issue(Lg, kt + 1, nxt);
-      cb.load(Rg, ldr_bytes, kt + 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    compute_ktile<T, TILE>(cur, cur + kOpBytes, fa, acc, [&] {
-      if (more) cb.store(nxt + kOpBytes);
-    });
-  } else {
-    // Always copy: the last k-tile reloads itself into the idle stage, so
-    // the step is one basic block the schedule below can order.
-    const int ktn = more ? kt + 1 : kt;
-    la.issue(Lg, ktn, nxt);
-    lb.issue(Rg, ktn, nxt + kOpBytes);
-    compute_ktile<T, TILE>(cur, cur + kOpBytes, fa, acc, [] {});
-    schedule_dma_ktile<T, TILE>();
+constexpr int kLdsBytes = 160 * 1024;
+
+template <int TM, int TN>
+struct Stages {
+  static constexpr int kNeed = (TM + TN) * kRowBytes;
+  static constexpr int kBytes = kNeed > 49152 ? 65536 : kNeed > 32768 ? 49152 : 32768;
+  static constexpr int kCount = 3 * kBytes <= kLdsBytes ? 3 : 2;
+  using M = StageMem<kBytes>;
+  static __device__ __forceinline__ char* s0() { return M::s0(); }
+  static __device__ __forceinline__ char* s1() { return M::s1(); }
+  static __device__ __forceinline__ char* s2() { return M::s2(); }
+};
+
+// Software pipeline over k-tiles.  With k-tile t in stage P and the stage D
+// free, one step
+//   1. starts the copies of k-tile t + (number of stages) into D,
+//   2. runs the MFMAs of substeps 2 and 3 of k-tile t (fragments already in
+//      registers) while reading substeps 0 and 1 of k-tile t+1 from P,
+//   3. runs the MFMAs of substeps 0 and 1 of k-tile t+1 while reading its
+//      substeps 2 and 3,
+//   4. waits for its reads and for the copies of k-tile t+2 and meets the
+//      other waves at the barrier.
+// The one barrier per k-tile thus sits between substeps 1 and 2, and the
+// fragment reads of one k-tile overlap the MFMAs of the previous one, so the
+// LDS and the matrix cores stay busy across the k-tile boundary.  Four
+// fragment sets (two substeps being consumed, two being read) live in
+// registers.
+template <int FM, int FN>
+struct FragSets {
+  Frags<FM, FN> f0, f1, f2, f3;
+};
+
+// Instruction order of one pipeline step (one basic block).  Each half
+// (two substeps of MFMAs) has NR read slots; slot i holds a few MFMAs, one
+// fragment read for the next two substeps and V_i copy instructions.  The
+// copies are spread out because the vector memory path takes about 16
+// cycles per 1 KiB copy instruction per compute unit: issued in one burst,
+// they would hold up the wave, and with it the MFMAs, for hundreds of
+// cycles.  With three stages the copies spread over the whole step (they
+// have two steps to land), with two over the first half.
+template <int NM, int NR, int NV, int I>
+__device__ __forceinline__ void schedule_half() {
+  if constexpr (I < NR) {
+    __builtin_amdgcn_sched_group_barrier(0x008, (I + 1) * NM / NR - I * NM / NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    constexpr int v = (I + 1) * NV / NR - I * NV / NR;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    schedule_half<NM, NR, NV, I + 1>();
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+}
+
+template <typename T, int TM, int TN>
+__device__ __forceinline__ void schedule_step() {
+  constexpr int FM = TM / 64, FN = TN / 64;
+  constexpr int NR = 2 * (FM + FN);                               // reads per half
+  constexpr int NM = 2 * FM * FN * (sizeof(T) == 4 ? 4 : 1);      // MFMAs per half
+  constexpr int NV = TM / 32 + TN / 32;                           // copies per step
+  constexpr int NV1 = Stages<TM, TN>::kCount == 3 ? (NV + 1) / 2 : NV;
+  static_assert(NM >= NR, "at least one MFMA per read");
+  schedule_half<NM, NR, NV1, 0>();
+  schedule_half<NM, NR, NV - NV1, 0>();
+}
+
+// Work-group barrier without the memory fence of __syncthreads(): that
+// fence waits for every load in flight, including the copies meant to stay
+// in flight across the barrier.  Every wait the LDS needs is explicit before
+// each call.  S_BARRIER has side effects, so the scheduler keeps memory
+// operations on their side of it; the empty asm does the same for the IR.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename T, int TM, int TN>
+__device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const DmaLoader<TM>& la,
+                                          const DmaLoader<TN>& lb, int kt_copy, char* __restrict__ D,
+                                          const char* __restrict__ P, const FragAddr& fa,
+                                          FragSets<TM / 64, TN / 64>& fs, f32x16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int FM = TM / 64, FN = TN / 64;
+  constexpr int kOffR = TM * kRowBytes;
+  la.issue(Lg, kt_copy, D);
+  lb.issue(Rg, kt_copy, D + kOffR);
+  load_frags<FM, FN>(P, P + kOffR, fa, 0, fs.f0);
+  load_frags<FM, FN>(P, P + kOffR, fa, 1, fs.f1);
+  mma_frags<T, FM, FN>(fs.f2, acc);
+  mma_frags<T, FM, FN>(fs.f3, acc);
+  load_frags<FM, FN>(P, P + kOffR, fa, 2, fs.f2);
+  load_frags<FM, FN>(P, P + kOffR, fa, 3, fs.f3);
+  mma_frags<T, FM, FN>(fs.f0, acc);
+  mma_frags<T, FM, FN>(fs.f1, acc);
+  schedule_step<T, TM, TN>();
+  // With three stages the copy just issued may stay in flight (it lands in
+  // a stage read two steps later); the one issued a step ago must be
+  // complete.
+  if constexpr (Stages<TM, TN>::kCount == 3)
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(TM / 32 + TN / 32));
+  else
+    __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
 }
 
 // acc += L-tile * R-tile^T over k-tiles [kt0, kt1) (acc is initialized by the
-// caller).
-template <typename T, int TILE, bool COL_RIGHT>
+// caller).  On return every copy has landed and all waves have passed a
+// barrier after their last LDS read, so the stage buffers may be reused.
+template <typename T, int TM, int TN>
 __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, const char* Rg, int64_t ldr_bytes,
-                                         int kt0, int kt1, Acc<T, TILE>& acc) {
-  constexpr int kOpBytes = TILE * kRowBytes;
+                                         int kt0, int kt1, Acc<T, TM, TN>& acc) {
+  constexpr int FM = TM / 64, FN = TN / 64;
+  constexpr int kOffR = TM * kRowBytes;
+  constexpr int kDma = TM / 32 + TN / 32;  // copy instructions per k-tile per wave
+  using S = Stages<TM, TN>;
+  constexpr int NS = S::kCount;
+  static_assert((TM + TN) * kRowBytes <= S::kBytes, "stage too small");
   const int w = threadIdx.x >> 6;
-  const int wr = (w >> 1) * (TILE / 2), wc = (w & 1) * (TILE / 2);
+  const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * (TN / 2);
   if (kt1 <= kt0) return;
+  const int klast = kt1 - 1;
+  auto clamp = [klast](int k) { return k < klast ? k : klast; };
 
-  char* s0 = Stages<TILE>::s0();
-  char* s1 = Stages<TILE>::s1();
   FragAddr fa;
   fa.init(wr, wc);
-  DmaLoader<TILE> la, lb;
+  DmaLoader<TM> la;
+  DmaLoader<TN> lb;
   la.init(ldl_bytes);
-  if constexpr (!COL_RIGHT) lb.init(ldr_bytes);
+  lb.init(ldr_bytes);
 
-  la.issue(Lg, kt0, s0);
-  if constexpr (COL_RIGHT) {
-    ColLoader<T, TILE> cb;
-    cb.load(Rg, ldr_bytes, kt0);
-    cb.store(s0 + kOpBytes);
+  // Prologue: k-tiles kt0, kt0+1 (and kt0+2 with three stages), clamped,
+  // into stages 0, 1 (and 2), then the MFMAs of substeps 0 and 1 of kt0.
+  la.issue(Lg, kt0, S::s0());
+  lb.issue(Rg, kt0, S::s0() + kOffR);
+  la.issue(Lg, clamp(kt0 + 1), S::s1());
+  lb.issue(Rg, clamp(kt0 + 1), S::s1() + kOffR);
+  if constexpr (NS == 3) {
+    la.issue(Lg, clamp(kt0 + 2), S::s2());
+    lb.issue(Rg, clamp(kt0 + 2), S::s2() + kOffR);
+  }
+  // Copies complete in order: wait for the first k-tile only.
+  __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * kDma));
+  lds_barrier();
+  FragSets<FM, FN> fs;
+  {
+    const char* s0 = S::s0();
+    load_frags<FM, FN>(s0, s0 + kOffR, fa, 0, fs.f0);
+    load_frags<FM, FN>(s0, s0 + kOffR, fa, 1, fs.f1);
+    load_frags<FM, FN>(s0, s0 + kOffR, fa, 2, fs.f2);
+    load_frags<FM, FN>(s0, s0 + kOffR, fa, 3, fs.f3);
+  }
+  mma_frags<T, FM, FN>(fs.f0, acc.v);
+  mma_frags<T, FM, FN>(fs.f1, acc.v);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NS - 2) * kDma));
+  lds_barrier();
+
+  // Step t copies k-tile t + NS into the stage of k-tile t and reads k-tile
+  // t + 1 from the next stage.  With three stages the loop is unrolled by
+  // three so that every step names its stages directly (the compiler then
+  // sees that a step's reads and its copies touch different objects).
+  auto step = [&](int t, char* D, const char* P) {
+    pipe_step<T, TM, TN>(Lg, Rg, la, lb, clamp(t + NS), D, P, fa, fs, acc.v);
+  };
+  if constexpr (NS == 3) {
+    int t = kt0;
+    for (; t + 3 <= klast; t += 3) {
+      step(t, S::s0(), S::s1());
+      step(t + 1, S::s1(), S::s2());
+      step(t + 2, S::s2(), S::s0());
+    }
+    if (t < klast) step(t++, S::s0(), S::s1());
+    if (t < klast) step(t, S::s1(), S::s2());
   } else {
-    lb.issue(Rg, kt0, s0 + kOpBytes);
+    for (int t = kt0; t < klast; ++t) {
+      const bool odd = (t - kt0) & 1;
+      step(t, odd ? S::s1() : S::s0(), odd ? S::s0() : S::s1());
+    }
   }
+  mma_frags<T, FM, FN>(fs.f2, acc.v);
+  mma_frags<T, FM, FN>(fs.f3, acc.v);
+  // The last copies (clamped repeats) must land before the caller reuses
+  // LDS.
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const bool odd = (kt - kt0) & 1;
-    ktile_step<T, TILE, COL_RIGHT>(Lg, Rg, ldr_bytes, la, lb, kt, kt + 1 < kt1, odd ? s1 : s0, odd ? s0 : s1, fa,
-                                   acc.v);
-  }
+  lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -414,21 +453,22 @@ struct SymArgs {
   int64_t sL, sR, sE, sC, sC2;  // batch strides in elements
   int ldk, ldn;      // row strides in elements
   int K;             // multiple of the k-tile
-  int tiles;         // n / TILE
+  int tiles;         // n / tile edge
   int n_real;
   float alpha_unused;
   float beta, gamma, delta;
 };
 
 template <typename T, typename OutT>
-struct NNArgs {
-  const T* B;        // n x n (ldb)
-  const T* X;        // n x m (ldx)
-  const T* E;        // n x m (ldx) or null when alpha == 0
-  OutT* Y;           // output
-  int64_t sB, sX, sE, sY;
-  int ldb, ldx;
-  int64_t ldy;       // output leading dimension
+struct NTArgs {
+  const T* B;        // n x n (ldb), left operand
+  const T* XT;       // X^T: m x n (ldxt), right operand
+  const T* E;        // X: n x m (lde), or null when alpha == 0
+  OutT* Y;           // output (internal: n x m, ld ldy; final: the caller's matrix)
+  T* YT;             // optional second internal output Y^T: m x n (ldyt)
+  int64_t sB, sXT, sE, sY, sYT;  // batch strides in elements
+  int ldb, ldxt, lde, ldyt;
+  int64_t ldy;
   int K;             // = n padded
   int tiles_m, tiles_n;
   int n_real, m_real;  // valid output rows/cols (wide orientation)
@@ -465,39 +505,48 @@ __device__ __forceinline__ void tri_tile(int idx, int nt, int& tm, int& tn) {
 }
 
 // Output tile staged in LDS (the stage buffers are free after the main
-// loop): TILE rows of TILE * sizeof(T) bytes, 16-byte chunk q of row r at
-// slot q ^ tswz(r).  The swizzle keeps both the row-quad writes from the
-// accumulators (32 consecutive rows) and the column reads of the mirrored
-// store (rows 8 apart) on distinct chunks.
-// The tile spans the two stage buffers: rows [0, kRowsPerStage) in the
-// first, the rest in the second.
-template <typename T, int TILE>
+// loop): TM rows of TN elements, each row at a power-of-two stride of
+// kRowB bytes (kSlots 16-byte slots, the first kCPR of them used), 16-byte
+// chunk q of row r at slot q ^ tswz(r).  The swizzle keeps both the
+// row-quad writes from the accumulators (32 consecutive rows) and the
+// column reads of the transposed stores (rows 8 apart) on distinct chunks.
+// The tile spans the first two stage buffers: rows [0, kRowsPerStage) in
+// the first, the rest in the second.
+template <typename T, int TM, int TN>
 struct TileLds {
-  static constexpr int kRowB = TILE * (int)sizeof(T);
-  static constexpr int kCPR = kRowB / 16;          // chunks per row
+  using S = Stages<TM, TN>;
+  static constexpr int kRowData = TN * (int)sizeof(T);
+  static constexpr int kRowB = kRowData <= 256 ? 256 : 512;
+  static constexpr int kSlots = kRowB / 16;
+  static constexpr int kCPR = kRowData / 16;       // chunks per row
   static constexpr int kEC = 16 / (int)sizeof(T);  // elements per chunk
-  static constexpr int kS = kCPR == 32 ? 5 : 4;
-  static constexpr int kStageB = 2 * TILE * kRowBytes;
-  static constexpr int kRowsPerStage = kStageB / kRowB;
-  static_assert(kCPR == 32 || kCPR == 16, "tile row must be 256 or 512 bytes");
-  static_assert(TILE <= 2 * kRowsPerStage, "tile must fit in the two stage buffers");
-  static __device__ __forceinline__ int tswz(int r) { return (r ^ (r >> kS)) & (kCPR - 1); }
+  static constexpr int kS = kSlots == 32 ? 5 : 4;
+  static constexpr int kRowsPerStage = S::kBytes / kRowB;
+  static_assert(kRowData <= 512, "tile row must fit in 512 bytes");
+  static_assert(TM <= 2 * kRowsPerStage, "tile must fit in the two stage buffers");
+  static __device__ __forceinline__ int tswz(int r) { return (r ^ (r >> kS)) & (kSlots - 1); }
   static __device__ __forceinline__ char* row_base(int r) {
-    return r < kRowsPerStage ? Stages<TILE>::s0() + r * kRowB : Stages<TILE>::s1() + (r - kRowsPerStage) * kRowB;
+    return r < kRowsPerStage ? S::s0() + r * kRowB : S::s1() + (r - kRowsPerStage) * kRowB;
   }
   static __device__ __forceinline__ char* at(int r, int col) {
     return row_base(r) + (((col / kEC) ^ tswz(r)) << 4) + (col % kEC) * (int)sizeof(T);
   }
   static __device__ __forceinline__ char* chunk(int r, int c) { return row_base(r) + ((c ^ tswz(r)) << 4); }
+  // kEC consecutive rows r0.. of column col, as one 16-byte chunk.
+  static __device__ __forceinline__ uint4 column_chunk(int r0, int col) {
+    T vals[kEC];
+#pragma unroll
+    for (int e = 0; e < kEC; ++e) vals[e] = *reinterpret_cast<const T*>(at(r0 + e, col));
+    return *reinterpret_cast<const uint4*>(vals);
+  }
 };
 
-template <typename T, int TILE>
-__device__ __forceinline__ void acc_zero(Acc<T, TILE>& acc) {
-  constexpr int FM = Acc<T, TILE>::FM;
+template <typename T, int TM, int TN>
+__device__ __forceinline__ void acc_zero(Acc<T, TM, TN>& acc) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+  for (int fm = 0; fm < Acc<T, TM, TN>::FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < FM; ++fn)
+    for (int fn = 0; fn < Acc<T, TM, TN>::FN; ++fn)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc.v[fm][fn][v] = 0.f;
 }
@@ -506,8 +555,9 @@ __device__ __forceinline__ void acc_zero(Acc<T, TILE>& acc) {
 // n x n products into their own kernel symbol, so profiles list them apart.
 template <typename T, int TILE, bool GRAM_INPUT>
 __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
-  constexpr int FM = Acc<T, TILE>::FM;
-  using TL = TileLds<T, TILE>;
+  using A = Acc<T, TILE, TILE>;
+  constexpr int FM = A::FM, FN = A::FN;
+  using TL = TileLds<T, TILE, TILE>;
   int tm, tn;
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
@@ -521,9 +571,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
   const bool diag_tile = (tm == tn);
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
-  Acc<T, TILE> acc;
-  acc_zero<T, TILE>(acc);
-  mainloop<T, TILE, false>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc);
+  A acc;
+  acc_zero(acc);
+  mainloop<T, TILE, TILE>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
@@ -536,7 +586,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
   for (int fm = 0; fm < FM; ++fm) {
     const int il = wr + fm * 32 + lr;
 #pragma unroll
-    for (int fn = 0; fn < FM; ++fn) {
+    for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int jl = wc + fn * 32 + 8 * g + 4 * h;
@@ -597,37 +647,37 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
   // of the mirror is column jj of the LDS tile.
   for (int q = threadIdx.x; q < kChunks; q += kThreads) {
     const int jj = q / TL::kCPR, c = q % TL::kCPR;
-    T vals[EC];
-#pragma unroll
-    for (int e = 0; e < EC; ++e) vals[e] = *reinterpret_cast<const T*>(TL::at(c * EC + e, jj));
-    const uint4 val = *reinterpret_cast<const uint4*>(vals);
+    const uint4 val = TL::column_chunk(c * EC, jj);
     *reinterpret_cast<uint4*>(C + (col0 + jj) * p.ldn + row0 + c * EC) = val;
     if (C2) *reinterpret_cast<uint4*>(C2 + (col0 + jj) * p.ldn + row0 + c * EC) = val;
   }
 }
 
-template <typename T, typename OutT, int TILE>
-__global__ void __launch_bounds__(kThreads, 1) k_nn(NNArgs<T, OutT> p) {
-  constexpr int FM = Acc<T, TILE>::FM;
-  using TL = TileLds<OutT, TILE>;
+// Y = alpha E + gamma B (X^T)^T on TM x TN tiles: the update of both forms.
+template <typename T, typename OutT, int TM, int TN>
+__global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
+  using A = Acc<T, TM, TN>;
+  constexpr int FM = A::FM, FN = A::FN;
+  using TL = TileLds<OutT, TM, TN>;
   const int tm = blockIdx.x / p.tiles_n;
   const int tn = blockIdx.x % p.tiles_n;
   const int bz = blockIdx.y;
   const int64_t ldb_bytes = (int64_t)p.ldb * sizeof(T);
-  const int64_t ldx_bytes = (int64_t)p.ldx * sizeof(T);
-  const char* Lg = reinterpret_cast<const char*>(p.B + bz * p.sB) + (int64_t)tm * TILE * ldb_bytes;
-  const char* Rg = reinterpret_cast<const char*>(p.X + bz * p.sX) + (int64_t)tn * TILE * sizeof(T);
+  const int64_t ldxt_bytes = (int64_t)p.ldxt * sizeof(T);
+  const char* Lg = reinterpret_cast<const char*>(p.B + bz * p.sB) + (int64_t)tm * TM * ldb_bytes;
+  const char* Rg = reinterpret_cast<const char*>(p.XT + bz * p.sXT) + (int64_t)tn * TN * ldxt_bytes;
   constexpr int BK = kRowBytes / sizeof(T);
   const T* E = p.E ? p.E + bz * p.sE : nullptr;
   OutT* Y = p.Y + bz * p.sY;
-  const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
-  Acc<T, TILE> acc;
-  acc_zero<T, TILE>(acc);
-  mainloop<T, TILE, true>(Lg, ldb_bytes, Rg, ldx_bytes, 0, p.K / BK, acc);
+  T* YT = p.YT ? p.YT + bz * p.sYT : nullptr;
+  const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
+  A acc;
+  acc_zero(acc);
+  mainloop<T, TM, TN>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
-  const int wr = (w >> 1) * (TILE / 2), wc = (w & 1) * (TILE / 2);
+  const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * (TN / 2);
   const float scale = p.final_out ? p.out_scale : 1.f;
   bool bad = false;
 
@@ -637,7 +687,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_nn(NNArgs<T, OutT> p) {
   for (int fm = 0; fm < FM; ++fm) {
     const int il = wr + fm * 32 + lr;
 #pragma unroll
-    for (int fn = 0; fn < FM; ++fn) {
+    for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int jl = wc + fn * 32 + 8 * g + 4 * h;
@@ -646,7 +696,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_nn(NNArgs<T, OutT> p) {
         v[1] = p.gamma * acc.v[fm][fn][4 * g + 1];
         v[2] = p.gamma * acc.v[fm][fn][4 * g + 2];
         v[3] = p.gamma * acc.v[fm][fn][4 * g + 3];
-        if (E) v += p.alpha * Quad<T>::load(E + (row0 + il) * p.ldx + col0 + jl);
+        if (E) v += p.alpha * Quad<T>::load(E + (row0 + il) * p.lde + col0 + jl);
         v *= scale;
         if (p.final_out) {
 #pragma unroll
@@ -658,45 +708,53 @@ __global__ void __launch_bounds__(kThreads, 1) k_nn(NNArgs<T, OutT> p) {
   }
   __syncthreads();
 
-  constexpr int kChunks = TILE * TL::kCPR;
+  constexpr int kEC = TL::kEC;
+  constexpr int kColChunks = TM / kEC;  // chunks of a tile column
   if (!p.final_out) {
-    // Internal buffer: whole padded tile, rows of 16-byte chunks.
-    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+    // Internal buffers: the whole padded tile, rows of Y and, when asked,
+    // rows of Y^T (columns of the tile).
+    for (int q = threadIdx.x; q < TM * TL::kCPR; q += kThreads) {
       const int r = q / TL::kCPR, c = q % TL::kCPR;
-      *reinterpret_cast<uint4*>(Y + (row0 + r) * p.ldy + col0 + c * TL::kEC) =
+      *reinterpret_cast<uint4*>(Y + (row0 + r) * p.ldy + col0 + c * kEC) =
           *reinterpret_cast<const uint4*>(TL::chunk(r, c));
+    }
+    if (YT) {
+      for (int q = threadIdx.x; q < TN * kColChunks; q += kThreads) {
+        const int jj = q / kColChunks, c = q % kColChunks;
+        *reinterpret_cast<uint4*>(YT + (col0 + jj) * p.ldyt + row0 + c * kEC) = TL::column_chunk(c * kEC, jj);
+      }
     }
   } else if (!p.transpose_out) {
     // Caller's matrix, same orientation: rows i < n_real, columns j < m_real.
-    const bool vec = (p.ldy % TL::kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
-    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+    const bool vec = (p.ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    for (int q = threadIdx.x; q < TM * TL::kCPR; q += kThreads) {
       const int r = q / TL::kCPR, c = q % TL::kCPR;
-      const int64_t i = row0 + r, j0 = col0 + c * TL::kEC;
+      const int64_t i = row0 + r, j0 = col0 + c * kEC;
       if (i >= p.n_real || j0 >= p.m_real) continue;
       const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
       OutT* dst = Y + i * p.ldy + j0;
-      if (vec && j0 + TL::kEC <= p.m_real) {
+      if (vec && j0 + kEC <= p.m_real) {
         *reinterpret_cast<uint4*>(dst) = val;
       } else {
         const OutT* vals = reinterpret_cast<const OutT*>(&val);
-        for (int e = 0; e < TL::kEC && j0 + e < p.m_real; ++e) dst[e] = vals[e];
+        for (int e = 0; e < kEC && j0 + e < p.m_real; ++e) dst[e] = vals[e];
       }
     }
   } else {
-    // Caller's matrix is the transpose: its row j holds tile column j.
-    const bool vec = (p.ldy % TL::kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
-    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
-      const int jj = q / TL::kCPR, c = q % TL::kCPR;
-      const int64_t j = col0 + jj, i0 = row0 + c * TL::kEC;
+    // Caller's matrix is the transpose: its row j holds tile column j, in
+    // TM / kEC chunks of kEC tile rows.
+    const bool vec = (p.ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    for (int q = threadIdx.x; q < TN * kColChunks; q += kThreads) {
+      const int jj = q / kColChunks, c = q % kColChunks;
+      const int64_t j = col0 + jj, i0 = row0 + c * kEC;
       if (j >= p.m_real || i0 >= p.n_real) continue;
-      OutT vals[TL::kEC];
-#pragma unroll
-      for (int e = 0; e < TL::kEC; ++e) vals[e] = *reinterpret_cast<const OutT*>(TL::at(c * TL::kEC + e, jj));
+      const uint4 val = TL::column_chunk(c * kEC, jj);
       OutT* dst = Y + j * p.ldy + i0;
-      if (vec && i0 + TL::kEC <= p.n_real) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
+      if (vec && i0 + kEC <= p.n_real) {
+        *reinterpret_cast<uint4*>(dst) = val;
       } else {
-        for (int e = 0; e < TL::kEC && i0 + e < p.n_real; ++e) dst[e] = vals[e];
+        const OutT* vals = reinterpret_cast<const OutT*>(&val);
+        for (int e = 0; e < kEC && i0 + e < p.n_real; ++e) dst[e] = vals[e];
       }
     }
   }

@@ -100,52 +100,64 @@ __global__ void __launch_bounds__(kStageThreads) k_scale(const double* partial, 
   if (threadIdx.x == 0) scale[blockIdx.x] = (float)((double)prescale / (sqrt(v) + (double)eps));
 }
 
-// Wide orientation, no transpose: X[i][j] = scale * M[i][j] for i < rows,
-// j < cols, zero elsewhere in the n_pad x m_pad buffer.  One block per
-// output row; each thread writes 16-byte groups.
+// Both layouts of the scaled, oriented, zero-padded matrix: X (n_pad x
+// m_pad, row-major) and X^T (m_pad x n_pad, row-major), one 64 x 64 block of
+// X per work-group.  The block of the caller's matrix that holds it (the X
+// block itself for a wide input, the X^T block for a tall one) is read with
+// 8-element row chunks into LDS; the same-orientation output is written from
+// rows of the LDS block and the other one from its columns, 16 bytes per
+// thread.  Elements outside the caller's matrix are zero.
 template <typename IO, typename T>
-__global__ void __launch_bounds__(kStageThreads) k_stage_rows(const IO* M, int64_t rows, int64_t cols, int64_t ld,
-                                                             int64_t bstride, const float* scales, T* X,
-                                                             int64_t m_pad, int64_t xstride) {
+__global__ void __launch_bounds__(kStageThreads) k_stage_pair(const IO* M, int64_t rows, int64_t cols, int64_t ld,
+                                                             int64_t bstride, int vec_ok, const float* scales, T* X,
+                                                             T* XT, int64_t n_pad, int64_t m_pad, int64_t xstride,
+                                                             int transposed, int blocks_j) {
+  constexpr int kB = 64, kV = 8;
+  __shared__ float tile[kB][kB + 1];
   const int b = blockIdx.y;
   const float scale = scales[b];
-  const int64_t i = blockIdx.x;
-  const IO* src = M + (int64_t)b * bstride + i * ld;
-  T* dst = X + (int64_t)b * xstride + i * m_pad;
-  constexpr int V = 16 / sizeof(T);
-  for (int64_t c0 = (int64_t)threadIdx.x * V; c0 < m_pad; c0 += (int64_t)kStageThreads * V) {
-    T out[V];
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const int64_t c = c0 + k;
-      const float x = (i < rows && c < cols) ? to_f32<IO>(src[c]) : 0.f;
-      out[k] = from_f32<T>(x * scale);
-    }
-    *reinterpret_cast<uint4*>(dst + c0) = *reinterpret_cast<const uint4*>(out);
-  }
-}
-
-// Tall input: X[i][j] = scale * M[j][i] (i < cols, j < rows), via a 64 x 64
-// LDS tile so both the read of M and the write of X are coalesced.
-template <typename IO, typename T>
-__global__ void __launch_bounds__(kStageThreads) k_stage_transpose(const IO* M, int64_t rows, int64_t cols, int64_t ld,
-                                                                  int64_t bstride, const float* scales, T* X,
-                                                                  int64_t m_pad, int64_t xstride, int tiles_j) {
-  __shared__ float tile[64][65];
-  const int b = blockIdx.y;
-  const float scale = scales[b];
-  const int64_t i0 = (int64_t)(blockIdx.x / tiles_j) * 64;  // X rows  = M cols
-  const int64_t j0 = (int64_t)(blockIdx.x % tiles_j) * 64;  // X cols  = M rows
+  const int64_t i0 = (int64_t)(blockIdx.x / blocks_j) * kB;  // X rows
+  const int64_t j0 = (int64_t)(blockIdx.x % blocks_j) * kB;  // X columns
+  // The caller's block: rows r0.., columns c0.. of M.
+  const int64_t r0 = transposed ? j0 : i0, c0 = transposed ? i0 : j0;
   const IO* src = M + (int64_t)b * bstride;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t mr = j0 + r, mc = i0 + tx;
-    tile[r][tx] = (mr < rows && mc < cols) ? to_f32<IO>(src[mr * ld + mc]) : 0.f;
+  for (int q = threadIdx.x; q < kB * (kB / kV); q += kStageThreads) {
+    const int r = q / (kB / kV), c = (q % (kB / kV)) * kV;
+    const int64_t mr = r0 + r, mc = c0 + c;
+    float v[kV];
+    if (vec_ok && mr < rows && mc + kV <= cols) {
+      const IO* p = src + mr * ld + mc;
+      IO e[kV];
+      if constexpr (sizeof(IO) == 2) {
+        *reinterpret_cast<uint4*>(e) = *reinterpret_cast<const uint4*>(p);
+      } else {
+        reinterpret_cast<uint4*>(e)[0] = reinterpret_cast<const uint4*>(p)[0];
+        reinterpret_cast<uint4*>(e)[1] = reinterpret_cast<const uint4*>(p)[1];
+      }
+#pragma unroll
+      for (int k = 0; k < kV; ++k) v[k] = to_f32<IO>(e[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kV; ++k) v[k] = (mr < rows && mc + k < cols) ? to_f32<IO>(src[mr * ld + mc + k]) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kV; ++k) tile[r][c + k] = v[k] * scale;
   }
   __syncthreads();
-  T* dst = X + (int64_t)b * xstride;
-  for (int r = ty; r < 64; r += 4) {
-    dst[(i0 + r) * m_pad + j0 + tx] = from_f32<T>(tile[tx][r] * scale);
+  // Same orientation as the block read: X for a wide input, X^T for a tall one.
+  T* direct = transposed ? XT + (int64_t)b * xstride + j0 * n_pad + i0 : X + (int64_t)b * xstride + i0 * m_pad + j0;
+  T* across = transposed ? X + (int64_t)b * xstride + i0 * m_pad + j0 : XT + (int64_t)b * xstride + j0 * n_pad + i0;
+  const int64_t ld_direct = transposed ? n_pad : m_pad, ld_across = transposed ? m_pad : n_pad;
+  constexpr int kE = 16 / sizeof(T);
+  for (int q = threadIdx.x; q < kB * (kB / kE); q += kStageThreads) {
+    const int r = q / (kB / kE), c = (q % (kB / kE)) * kE;
+    T out[kE];
+#pragma unroll
+    for (int k = 0; k < kE; ++k) out[k] = from_f32<T>(tile[r][c + k]);
+    *reinterpret_cast<uint4*>(direct + r * ld_direct + c) = *reinterpret_cast<const uint4*>(out);
+#pragma unroll
+    for (int k = 0; k < kE; ++k) out[k] = from_f32<T>(tile[c + k][r]);
+    *reinterpret_cast<uint4*>(across + r * ld_across + c) = *reinterpret_cast<const uint4*>(out);
   }
 }
 

@@ -57,28 +57,65 @@ def test_options_defaults():
     assert opt.restart_mask == 1 << 4
     assert abs(opt.eps - 1e-7) < 1e-12
     assert opt.internal == -1 and not opt.d_status
+    assert opt.tile == 0
 
 
 def test_workspace_size_layout():
-    # Standard: partial sums + 2 X buffers + 2 n x n buffers (fp16 internal).
-    ws = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "standard")
+    # Standard: partial sums + 2 pairs of X and X^T buffers + 2 n x n
+    # buffers (fp16 internal).
+    ws = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "standard",
+                            tile=256)
     x = 4096 * 14336 * 2
     nn = 4096 * 4096 * 2
-    assert 2 * x + 2 * nn <= ws <= 2 * x + 2 * nn + 16384
-    wg = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "gram")
+    assert 4 * x + 2 * nn <= ws <= 4 * x + 2 * nn + 16384
+    wg = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "gram", tile=256)
     assert wg - ws == pytest.approx(2 * nn, abs=1024)
+    # Tile 192: n and m are padded to multiples of 192 (4224 and 14400).
+    w192 = nsa.workspace_size(4096, 14336, 1, torch.bfloat16, "standard",
+                              tile=192)
+    x192, nn192 = 4224 * 14400 * 2, 4224 * 4224 * 2
+    assert 4 * x192 + 2 * nn192 <= w192 <= 4 * x192 + 2 * nn192 + 16384
     # Tall input has the same workspace as its transpose.
-    assert nsa.workspace_size(14336, 4096) == ws
+    assert nsa.workspace_size(14336, 4096) == nsa.workspace_size(4096, 14336)
     # Ragged sizes are padded to the tile edge (128 below 512 rows).
     w = nsa.workspace_size(200, 300, 1, torch.float16, "standard")
-    assert w >= 2 * 256 * 384 * 2 + 2 * 256 * 256 * 2
+    assert w >= 4 * 256 * 384 * 2 + 2 * 256 * 256 * 2
     # fp32 doubles the buffers.
     assert nsa.workspace_size(256, 1024, 1, torch.float32) > \
         nsa.workspace_size(256, 1024, 1, torch.bfloat16)
     # Batches scale linearly.
-    one = nsa.workspace_size(2048, 1408, 1, torch.bfloat16, "gram")
-    many = nsa.workspace_size(2048, 1408, 128, torch.bfloat16, "gram")
+    one = nsa.workspace_size(2048, 1408, 1, torch.bfloat16, "gram", tile=256)
+    many = nsa.workspace_size(2048, 1408, 128, torch.bfloat16, "gram",
+                              tile=256)
     assert 127 * one < many <= 128 * one
+
+
+def _padded_n(rows, cols, batch=1, mode="gram"):
+    """n_pad the automatic tile choice gives, read off the workspace size."""
+    n = min(rows, cols)
+    ws = nsa.workspace_size(rows, cols, batch, torch.bfloat16, mode)
+    for tile in (128, 192, 256):
+        if nsa.workspace_size(rows, cols, batch, torch.bfloat16, mode,
+                              tile=tile) == ws:
+            return tile
+    raise AssertionError(f"no forced tile reproduces the automatic plan for {n}")
+
+
+def test_automatic_tile_choice():
+    # 4096 x 4096 symmetric products: 253 tiles of 192 fill the 256 compute
+    # units where 136 tiles of 256 leave half of them idle.
+    assert _padded_n(4096, 14336) == 192
+    # Small matrices use 128.
+    assert _padded_n(300, 500) == 128
+    # Forced tiles: fp32 products take 128 only; unknown edges are refused.
+    lib = B.lib()
+    for tile in (64, 200, 512):
+        opt = B.make_options(tile=tile)
+        assert lib.ns_workspace_size(512, 512, 1, B.NS_BF16, 0,
+                                     ctypes.byref(opt)) == 0
+    opt = B.make_options(tile=192)
+    assert lib.ns_workspace_size(512, 512, 1, B.NS_FP32, 0,
+                                 ctypes.byref(opt)) == 0
 
 
 def test_workspace_size_rejects_bad_arguments():

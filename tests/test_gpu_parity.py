@@ -47,7 +47,7 @@ def _oracle(m64, mode, steps=5, abc=TUNED, mask=1 << 4, eps=1e-7):
 
 
 def _run(m_cpu, mode, steps=5, abc=TUNED, mask=1 << 4, internal=None,
-         ld_pad=0):
+         ld_pad=0, tile=0):
     dev = _dev()
     rows, cols = m_cpu.shape
     if ld_pad:
@@ -57,7 +57,7 @@ def _run(m_cpu, mode, steps=5, abc=TUNED, mask=1 << 4, internal=None,
     else:
         x = m_cpu.to(dev)
     nsa.orthogonalize(x, steps=steps, abc=abc, mode=mode, restart_mask=mask,
-                      internal=internal)
+                      internal=internal, tile=tile)
     torch.cuda.synchronize()
     return x.double().cpu().numpy()
 
@@ -199,6 +199,31 @@ def test_parity_large_ragged(shape, mode):
     err = _rel(_run(m, mode), _oracle(m.double().numpy(), mode))
     print(f"{shape} {mode}: rel err {err:.3e}")
     assert err < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# Every tile edge, forced: several tiles and a ragged tail in each direction.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tile", [128, 192, 256])
+@pytest.mark.parametrize("shape", [(700, 1300), (1300, 700), (384, 384)])
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+def test_parity_forced_tile(tile, shape, mode):
+    m = workloads.column_scaled(shape[0], shape[1], seed=41, dtype="bf16")
+    err = _rel(_run(m, mode, tile=tile), _oracle(m.double().numpy(), mode))
+    print(f"{shape} {mode} tile {tile}: rel err {err:.3e}")
+    assert err < 1e-2
+
+
+@pytest.mark.parametrize("tile", [128, 192, 256])
+def test_forced_tile_fp16_input_bf16_products(tile):
+    m = workloads.gaussian((520, 900), seed=42, dtype="fp16")
+    err = _rel(_run(m, "gram", internal="bf16", tile=tile),
+               _oracle(m.double().numpy(), "gram"))
+    print(f"fp16 in, bf16 products, tile {tile}: rel err {err:.3e}")
+    # bf16 products keep 8 mantissa bits, so the bar is looser than for fp16
+    # products; a tile indexing mistake gives errors of order one.
+    assert err < 3e-2
 
 
 # ---------------------------------------------------------------------------
