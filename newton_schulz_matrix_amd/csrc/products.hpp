@@ -504,6 +504,19 @@ __device__ __forceinline__ void tri_tile(int idx, int nt, int& tm, int& tn) {
   }
 }
 
+// Full tile grids (the update) in groups of kGroupRows tile rows: within a
+// group the list runs down the columns, tile row fastest, so the 32 or so
+// work-groups an XCD runs at a time cover a 4 x 8 block of tiles and share
+// 4 row panels of B and 8 row panels of X^T in its L2.
+constexpr int kGroupRows = 4;
+__device__ __forceinline__ void grouped_tile(int idx, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupRows * tiles_n;
+  const int g = idx / per_group, within = idx % per_group;
+  const int rows = tiles_m - g * kGroupRows < kGroupRows ? tiles_m - g * kGroupRows : kGroupRows;
+  tn = within / rows;
+  tm = g * kGroupRows + within % rows;
+}
+
 // Output tile staged in LDS (the stage buffers are free after the main
 // loop): TM rows of TN elements, each row at a power-of-two stride of
 // kRowB bytes (kSlots 16-byte slots, the first kCPR of them used), 16-byte
@@ -659,8 +672,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
   using A = Acc<T, TM, TN>;
   constexpr int FM = A::FM, FN = A::FN;
   using TL = TileLds<OutT, TM, TN>;
-  const int tm = blockIdx.x / p.tiles_n;
-  const int tn = blockIdx.x % p.tiles_n;
+  int tm, tn;
+  if (gridDim.y == 1) {
+    grouped_tile(xcd_order(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
+  } else {
+    tm = blockIdx.x / p.tiles_n;
+    tn = blockIdx.x % p.tiles_n;
+  }
   const int bz = blockIdx.y;
   const int64_t ldb_bytes = (int64_t)p.ldb * sizeof(T);
   const int64_t ldxt_bytes = (int64_t)p.ldxt * sizeof(T);
