@@ -217,6 +217,9 @@ struct Runner {
   Tracer tr;
 
   T* xbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_x[i]); }
+  // Length of a contraction over `real` rows or columns: a whole number of
+  // k-tiles (64 16-bit or 32 fp32 elements).
+  static int64_t k_extent(int64_t real) { return round_up(real, kRowBytes / (int64_t)sizeof(T)); }
   T* xtbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_xt[i]); }
   T* nnbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_nn[i]); }
 
@@ -279,7 +282,7 @@ struct Runner {
     a.lde = (int)p.m_pad;
     a.ldyt = (int)p.n_pad;
     a.ldy = p.m_pad;
-    a.K = (int)p.n_pad;
+    a.K = (int)k_extent(p.n);
     a.tiles_m = (int)(p.n_pad / TILE);
     a.tiles_n = (int)(p.m_pad / nn_tile_n(TILE));
     a.n_real = (int)p.n;
@@ -315,7 +318,7 @@ struct Runner {
     a.lde = (int)p.m_pad;
     a.ldyt = 0;
     a.ldy = ld;
-    a.K = (int)p.n_pad;
+    a.K = (int)k_extent(p.n);
     a.tiles_m = (int)(p.n_pad / TILE);
     a.tiles_n = (int)(p.m_pad / nn_tile_n(TILE));
     a.n_real = (int)p.n;
@@ -364,6 +367,9 @@ struct Runner {
     const float unscale = ldexpf(1.f, -pe);
     const float gram_scale = ldexpf(1.f, -2 * pe);
     const int mp = (int)p.m_pad, np = (int)p.n_pad;
+    // Contractions stop at the real size rounded up to the k-tile: the padded
+    // rows and columns of X and of every n x n matrix are exactly zero.
+    const int km = (int)k_extent(p.m), kn = (int)k_extent(p.n);
     hipError_t e = stage(prescale, eps);
     if (e != hipSuccess) return e;
     int xi = 0;
@@ -372,8 +378,8 @@ struct Runner {
       T* B = nnbuf(1);
       for (int k = 0; k < steps; ++k) {
         T* X = xbuf(xi);
-        if ((e = sym<TILE>(X, X, mp, mp, nullptr, 0.f, gram_scale, A, nullptr, 0.f)) != hipSuccess) return e;
-        if ((e = sym<TILE>(A, A, np, np, A, b[k], c[k], B, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(X, X, km, mp, nullptr, 0.f, gram_scale, A, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(A, A, kn, np, A, b[k], c[k], B, nullptr, 0.f)) != hipSuccess) return e;
         if (k + 1 < steps) {
           if ((e = nn_internal<TILE>(B, xi, true, a[k], xi ^ 1)) != hipSuccess) return e;
           xi ^= 1;
@@ -389,30 +395,30 @@ struct Runner {
     T* Z = nnbuf(1);
     T* Qb[2] = {nnbuf(2), nnbuf(3)};
     int qi = 0;
-    if ((e = sym<TILE>(xbuf(0), xbuf(0), mp, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f)) != hipSuccess) return e;
+    if ((e = sym<TILE>(xbuf(0), xbuf(0), km, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f)) != hipSuccess) return e;
     bool fresh = true;
     for (int k = 1; k <= steps; ++k) {
       if (k > 1 && ((mask >> k) & 1u)) {
         if ((e = nn_internal<TILE>(Qb[qi], xi, false, 0.f, xi ^ 1)) != hipSuccess) return e;
         xi ^= 1;
-        if ((e = sym<TILE>(xbuf(xi), xbuf(xi), mp, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f)) != hipSuccess)
+        if ((e = sym<TILE>(xbuf(xi), xbuf(xi), km, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f)) != hipSuccess)
           return e;
         fresh = true;
       }
       const float ak = a[k - 1], bk = b[k - 1], ck = c[k - 1];
       // Z' = b R + c R^2; at a fresh start Q = a I + Z' comes out of the same
       // epilogue.
-      if ((e = sym<TILE>(R, R, np, np, R, bk, ck, Z, fresh ? Qb[qi] : nullptr, ak)) != hipSuccess) return e;
+      if ((e = sym<TILE>(R, R, kn, np, R, bk, ck, Z, fresh ? Qb[qi] : nullptr, ak)) != hipSuccess) return e;
       if (!fresh) {
-        if ((e = sym<TILE>(Z, Qb[qi], np, np, Qb[qi], ak, 1.f, Qb[qi ^ 1], nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(Z, Qb[qi], kn, np, Qb[qi], ak, 1.f, Qb[qi ^ 1], nullptr, 0.f)) != hipSuccess) return e;
         qi ^= 1;
       }
       fresh = false;
       const bool need_r = k < steps && !((mask >> (k + 1)) & 1u);
       if (need_r) {
         T* V = Qb[qi ^ 1];
-        if ((e = sym<TILE>(Z, R, np, np, R, ak, 1.f, V, nullptr, 0.f)) != hipSuccess) return e;
-        if ((e = sym<TILE>(Z, V, np, np, V, ak, 1.f, R, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(Z, R, kn, np, R, ak, 1.f, V, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(Z, V, kn, np, V, ak, 1.f, R, nullptr, 0.f)) != hipSuccess) return e;
       }
     }
     return nn_final<TILE>(Qb[qi], xi, false, 0.f, unscale);

@@ -564,6 +564,46 @@ __device__ __forceinline__ void acc_zero(Acc<T, TM, TN>& acc) {
       for (int v = 0; v < 16; ++v) acc.v[fm][fn][v] = 0.f;
 }
 
+// The epilogue's E operand (the "alpha E +" / "beta E +" term) in the
+// accumulator layout: lane (lr, h) of wave (wr, wc) needs E[il][jl..jl+3]
+// for il = wr + 32 fm + lr, jl = wc + 32 fn + 8 g + 4 h.  Tiles up to 192
+// have the registers to load it (8 bytes per (fm, fn, g)) before the main
+// loop, so its latency and its burst of HBM reads overlap the MFMAs instead
+// of sitting between the last MFMA and the stores; the 256 tile loads it in
+// the epilogue.
+template <typename T, int TM, int TN>
+struct EPrefetch {
+  static constexpr int FM = TM / 64, FN = TN / 64;
+  static constexpr bool kEnabled = FM * FN <= 9 && sizeof(T) == 2;
+  uint2 v[kEnabled ? FM : 1][kEnabled ? FN : 1][4];
+  __device__ __forceinline__ void load(const T* E, int64_t ld, int64_t row0, int64_t col0) {
+    if constexpr (kEnabled) {
+      if (!E) return;
+      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+      const int lr = lane & 31, h = lane >> 5;
+      const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * (TN / 2);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            v[fm][fn][g] = *reinterpret_cast<const uint2*>(E + (row0 + wr + fm * 32 + lr) * ld + col0 + wc +
+                                                           fn * 32 + 8 * g + 4 * h);
+    }
+  }
+  // E[il][jl..jl+3] as floats: from the registers, or loaded now.
+  __device__ __forceinline__ f32x4 get(const T* E, int64_t ld, int64_t row0, int64_t col0, int il, int jl, int fm,
+                                       int fn, int g) const {
+    if constexpr (kEnabled) {
+      const T* e = reinterpret_cast<const T*>(&v[fm][fn][g]);
+      return f32x4{to_f32<T>(e[0]), to_f32<T>(e[1]), to_f32<T>(e[2]), to_f32<T>(e[3])};
+    } else {
+      return Quad<T>::load(E + (row0 + il) * ld + col0 + jl);
+    }
+  }
+};
+
 // GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
 // n x n products into their own kernel symbol, so profiles list them apart.
 template <typename T, int TILE, bool GRAM_INPUT>
@@ -584,6 +624,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
   const bool diag_tile = (tm == tn);
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  EPrefetch<T, TILE, TILE> ep;
+  ep.load(E, p.ldn, row0, col0);
   A acc;
   acc_zero(acc);
   mainloop<T, TILE, TILE>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc);
@@ -608,7 +650,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
         v[1] = p.gamma * acc.v[fm][fn][4 * g + 1];
         v[2] = p.gamma * acc.v[fm][fn][4 * g + 2];
         v[3] = p.gamma * acc.v[fm][fn][4 * g + 3];
-        if (E) v += p.beta * Quad<T>::load(E + (row0 + il) * p.ldn + col0 + jl);
+        if (E) v += p.beta * ep.get(E, p.ldn, row0, col0, il, jl, fm, fn, g);
         Quad<T>::store(reinterpret_cast<T*>(TL::at(il, jl)), v);
         if (C2 && diag_tile) {
 #pragma unroll
@@ -689,6 +731,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
   OutT* Y = p.Y + bz * p.sY;
   T* YT = p.YT ? p.YT + bz * p.sYT : nullptr;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
+  EPrefetch<T, TM, TN> ep;
+  ep.load(E, p.lde, row0, col0);
   A acc;
   acc_zero(acc);
   mainloop<T, TM, TN>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc);
@@ -714,7 +758,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
         v[1] = p.gamma * acc.v[fm][fn][4 * g + 1];
         v[2] = p.gamma * acc.v[fm][fn][4 * g + 2];
         v[3] = p.gamma * acc.v[fm][fn][4 * g + 3];
-        if (E) v += p.alpha * Quad<T>::load(E + (row0 + il) * p.lde + col0 + jl);
+        if (E) v += p.alpha * ep.get(E, p.lde, row0, col0, il, jl, fm, fn, g);
         v *= scale;
         if (p.final_out) {
 #pragma unroll
