@@ -22,8 +22,11 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,6 +38,10 @@ METRIC = ("NS orthogonalizations/sec + TFLOP/s (MFMA % of peak) at "
           "4096x14336 bf16")
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# Sources whose change invalidates a committed HBM-traffic measurement.
+KERNEL_SOURCES = ["newton_schulz_matrix_amd/csrc/products.hpp",
+                  "newton_schulz_matrix_amd/csrc/stage.hpp",
+                  "newton_schulz_matrix_amd/csrc/api.hip"]
 
 
 def parse():
@@ -170,21 +177,60 @@ def run_form(x, mode, steps, warmup, args, trace_kinds=None):
         mask |= 1 << KERNEL_KINDS.index(k)
     ev = Events(2 * per_call * steps)
     tr = make_trace(ev, per_call * steps, mask)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    # An event at every step boundary: the first and last bracket the timed
+    # region, consecutive pairs give per-call times.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
+    marks[0].record()
+    for i in range(steps):
         call(x, trace=tr, **kw)
-    stop.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(stop)
+    total_ms = marks[0].elapsed_time(marks[-1])
+    per_call = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+
+    def pct(q):
+        return per_call[min(len(per_call) - 1, int(q * (len(per_call) - 1) + 0.5))]
+
     timed = trace_stats(ev, tr)
     ev.close()
     return {"ms_per_step": total_ms / steps, "wall_s": wall,
+            "ms_p10": pct(0.1), "ms_p50": pct(0.5), "ms_p90": pct(0.9),
             "dominant": dominant, "warm_kernels": warm, "timed_kernels": timed}
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kind, workload, mode, tile):
+    """HBM bytes per launch of `kind` from the rocprofv3 counter summaries.
+
+    A summary in profiles/ carries lines
+      traffic: kind=K workload=W mode=M tile=T fetch_bytes=F write_bytes=B sources=H
+    (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a plain copy's
+    readings).  They count only while H matches the current kernel sources.
+    """
+    digest = sources_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(re.findall(r"(\w+)=(\S+)", line))
+                if (kv.get("kind") == kind and kv.get("workload") == workload
+                        and kv.get("mode") == mode
+                        and kv.get("tile") == str(tile)
+                        and kv.get("sources") == digest):
+                    return (float(kv["fetch_bytes"]) + float(kv["write_bytes"]),
+                            os.path.relpath(path, ROOT))
+    return None, None
 
 
 def cpu_baseline(m_cpu, mode, restart_mask):
@@ -193,20 +239,26 @@ def cpu_baseline(m_cpu, mode, restart_mask):
     from threadpoolctl import threadpool_info
     m64 = m_cpu.double().numpy()
     restarts = tuple(k for k in range(1, 33) if (restart_mask >> k) & 1)
-    t0 = time.perf_counter()
-    if mode == "gram":
-        oracle.ns_gram(m64, 5, oracle.TUNED_ABC, restarts)
-    else:
-        oracle.ns_standard(m64, 5, oracle.TUNED_ABC)
-    dt = time.perf_counter() - t0
+
+    def once():
+        t0 = time.perf_counter()
+        if mode == "gram":
+            oracle.ns_gram(m64, 5, oracle.TUNED_ABC, restarts)
+        else:
+            oracle.ns_standard(m64, 5, oracle.TUNED_ABC)
+        return time.perf_counter() - t0
+
+    once()                                    # warm-up (BLAS threads, caches)
+    times = sorted(once() for _ in range(3))
+    dt = times[1]
     threads = [d.get("num_threads") for d in threadpool_info()
                if d.get("user_api") == "blas"]
     cores = int(max(threads)) if threads else len(os.sched_getaffinity(0))
     return {"value": 1.0 / dt, "unit": "orth/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"one full {m64.shape[0]}x{m64.shape[1]} {mode}-form "
-                      f"orthogonalization in fp64 (numpy/OpenBLAS), "
-                      f"{dt:.1f} s"}
+            "sample": f"full {m64.shape[0]}x{m64.shape[1]} {mode}-form "
+                      f"orthogonalizations in fp64 (numpy/OpenBLAS): median "
+                      f"of 3 after 1 warm-up, {dt:.1f} s each"}
 
 
 def copy_calibration(args):
@@ -276,7 +328,11 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved,
                 "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    traffic, traffic_src = committed_traffic(dom, args.workload, args.mode,
+                                             args.tile or "auto")
+    roof["traffic"] = traffic
+    if traffic_src:
+        roof["traffic_source"] = traffic_src
     roof["kernel"] = dom
     roof["avg_launch_ms"] = avg_ms
     roof["launches_timed"] = ks["launches"]
@@ -300,6 +356,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_p10_p50_p90": [res["ms_p10"], res["ms_p50"], res["ms_p90"]],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -44,7 +44,7 @@ struct Plan {
 };
 
 // Columns of the update tiles that go with a square tile edge: square tiles
-// where three pipeline stages fit in LDS (128, 192), 256 otherwise.
+// (192 x 256 update tiles were measured slower than 192 x 192 at 4096 x 14336).
 constexpr int nn_tile_n(int edge) { return edge; }
 
 bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
