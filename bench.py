@@ -8,6 +8,12 @@ every product, and the final cast back into the caller's buffer.  The call
 works in place, so each step orthogonalizes the previous step's output; the
 products are dense, so the work does not depend on the values.
 
+Other workloads (--workload): the transposed and square Llama shapes, the
+MoE expert batch (128 x 2048 x 1408 and transposed), the NanoGPT-124M
+weight set (three batched calls per step), the ROOT split of a 2048 x 8192
+Student-t gradient followed by orthogonalization of its robust part, and a
+256 x 1024 fp32 matrix.  `value` counts matrices per second.
+
 Prints one JSON line.  Besides the driver's fields it carries:
   tflops / mfma_frac     algorithmic (symmetric-aware) TFLOP/s of the whole
                          step and its fraction of the fp16/bf16 dense peak;
@@ -52,6 +58,7 @@ def parse():
     ap.add_argument("--workload", default="llama8b-mlp",
                     choices=["llama8b-mlp", "llama8b-down", "llama8b-square",
                              "moe-experts", "moe-experts-t", "small-fp32",
+                             "nanogpt-set", "root-split",
                              "copy-calibration"])
     ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
     ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
@@ -65,19 +72,30 @@ def parse():
 
 
 def workload_input(name):
+    """(list of host input tensors, I/O dtype name, ROOT split first?).
+
+    A 3-D tensor is one batched call; a list of several tensors is run as
+    one call each, in order, per step.
+    """
     import workloads
     if name == "llama8b-mlp":
-        return workloads.llama8b((4096, 14336)), "bf16"
+        return [workloads.llama8b((4096, 14336))], "bf16", False
     if name == "llama8b-down":
-        return workloads.llama8b((14336, 4096)), "bf16"
+        return [workloads.llama8b((14336, 4096))], "bf16", False
     if name == "llama8b-square":
-        return workloads.llama8b((4096, 4096)), "bf16"
+        return [workloads.llama8b((4096, 4096))], "bf16", False
     if name == "moe-experts":
-        return workloads.moe_experts(128, 2048, 1408), "bf16"
+        return [workloads.moe_experts(128, 2048, 1408)], "bf16", False
     if name == "moe-experts-t":
-        return workloads.moe_experts(128, 1408, 2048), "bf16"
+        return [workloads.moe_experts(128, 1408, 2048)], "bf16", False
     if name == "small-fp32":
-        return workloads.small_fp32(), "fp32"
+        return [workloads.small_fp32()], "fp32", False
+    if name == "nanogpt-set":
+        import torch
+        groups = workloads.nanogpt_set()
+        return [torch.stack(g) for g in groups.values()], "bf16", False
+    if name == "root-split":
+        return [workloads.heavy_tailed()], "bf16", True
     raise ValueError(name)
 
 
@@ -142,30 +160,52 @@ def trace_stats(events, t):
     return stats
 
 
-def run_form(x, mode, steps, warmup, args, trace_kinds=None):
-    """Warm up, then time `steps` calls; optionally trace some kernel kinds."""
+def make_step(inputs, mode, args, split):
+    """A closure running one step: every input once (after the split)."""
     import torch
     import newton_schulz_matrix_amd as nsa
-    batched = x.dim() == 3
-    call = nsa.orthogonalize_batched if batched else nsa.orthogonalize
-    rows, cols = x.shape[-2], x.shape[-1]
-    ws = torch.empty(nsa.workspace_size(rows, cols, x.shape[0] if batched
-                                        else 1, x.dtype, mode,
-                                        args.restart_mask, args.internal,
-                                        args.tile)
-                     + 256, dtype=torch.uint8, device=x.device)
-    kw = dict(mode=mode, restart_mask=args.restart_mask,
-              internal=args.internal, workspace=ws, tile=args.tile)
-    # One untraced call first: the first launch of each kernel also loads
-    # its code object.  Then warm-up calls with every kind traced, to find
+    calls = []
+    for x in inputs:
+        batched = x.dim() == 3
+        fn = nsa.orthogonalize_batched if batched else nsa.orthogonalize
+        rows, cols = x.shape[-2], x.shape[-1]
+        ws = torch.empty(nsa.workspace_size(rows, cols, x.shape[0] if batched
+                                            else 1, x.dtype, mode,
+                                            args.restart_mask, args.internal,
+                                            args.tile)
+                         + 256, dtype=torch.uint8, device=x.device)
+        kw = dict(mode=mode, restart_mask=args.restart_mask,
+                  internal=args.internal, workspace=ws, tile=args.tile)
+        # The ROOT split reads the original gradient and writes B into the
+        # buffer the orthogonalization then works on in place.
+        src = x.clone() if split else None
+        calls.append((fn, x, kw, src))
+
+    def step(trace=None):
+        for fn, x, kw, src in calls:
+            if src is not None:
+                nsa.soft_threshold_split(src, out_b=x)
+            if trace is None:
+                fn(x, **kw)
+            else:
+                fn(x, trace=trace, **kw)
+    return step
+
+
+def run_form(inputs, mode, steps, warmup, args, split=False, trace_kinds=None):
+    """Warm up, then time `steps` steps; optionally trace some kernel kinds."""
+    import torch
+    step = make_step(inputs, mode, args, split)
+    # One untraced step first: the first launch of each kernel also loads
+    # its code object.  Then warm-up steps with every kind traced, to find
     # the dominant kernel.
-    call(x, **kw)
+    step()
     torch.cuda.synchronize()
-    per_call = 64
+    per_call = 64 * len(inputs)
     ev = Events(2 * per_call * max(warmup, 1))
     tr = make_trace(ev, per_call * max(warmup, 1), 0xFFFFFFFF)
     for _ in range(max(warmup, 1)):
-        call(x, trace=tr, **kw)
+        step(tr)
     torch.cuda.synchronize()
     warm = trace_stats(ev, tr)
     ev.close()
@@ -184,7 +224,7 @@ def run_form(x, mode, steps, warmup, args, trace_kinds=None):
     t0 = time.perf_counter()
     marks[0].record()
     for i in range(steps):
-        call(x, trace=tr, **kw)
+        step(tr)
         marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -303,17 +343,22 @@ def main():
     from newton_schulz_matrix_amd.flops import ns_flops
 
     dev = torch.device("cuda:0")
-    m_cpu, io = workload_input(args.workload)
-    x = m_cpu.to(dev)
-    rows, cols = x.shape[-2], x.shape[-1]
-    batch = x.shape[0] if x.dim() == 3 else 1
+    host_inputs, io, split = workload_input(args.workload)
+    inputs = [m.to(dev) for m in host_inputs]
+    shapes = [(m.shape[0] if m.dim() == 3 else 1, m.shape[-2], m.shape[-1])
+              for m in host_inputs]
+    matrices = sum(b for b, _, _ in shapes)
     internal = args.internal or ("fp16" if io != "fp32" else "fp32")
     dtype = {"fp16": "f16", "bf16": "bf16", "fp32": "f32"}[internal]
 
-    res = run_form(x, args.mode, args.steps, args.warmup, args)
+    def total_flops(mode):
+        return sum(b * ns_flops(r, c, 5, mode, args.restart_mask)
+                   for b, r, c in shapes)
+
+    res = run_form(inputs, args.mode, args.steps, args.warmup, args, split)
     ms = res["ms_per_step"]
-    flops = batch * ns_flops(rows, cols, 5, args.mode, args.restart_mask)
-    value = batch * 1000.0 / ms
+    flops = total_flops(args.mode)
+    value = matrices * 1000.0 / ms
     tflops = flops / (ms * 1e-3) / 1e12
 
     dom = res["dominant"]
@@ -362,8 +407,11 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "rows": rows, "cols": cols,
-                   "batch": batch, "io_dtype": io, "mode": args.mode,
+        "config": {"workload": args.workload,
+                   "shapes": [f"{b}x{r}x{c}" for b, r, c in shapes],
+                   "rows": shapes[0][1], "cols": shapes[0][2],
+                   "batch": matrices, "io_dtype": io, "mode": args.mode,
+                   "root_split": split,
                    "ns_steps": 5, "abc": list(nsa.TUNED_ABC),
                    "restart_mask": args.restart_mask,
                    "tile": args.tile or "auto",
@@ -374,18 +422,20 @@ def main():
         "kernels": kernels,
     }
     if not args.no_standard and args.mode == "gram":
-        std = run_form(x, "standard", max(args.steps // 2, 3), 2, args)
-        sflops = batch * ns_flops(rows, cols, 5, "standard")
+        std = run_form(inputs, "standard", max(args.steps // 2, 3), 2, args,
+                       split)
         out["standard_form"] = {
             "ms_per_step": std["ms_per_step"],
-            "orth_per_s": batch * 1000.0 / std["ms_per_step"],
-            "tflops": sflops / (std["ms_per_step"] * 1e-3) / 1e12,
+            "orth_per_s": matrices * 1000.0 / std["ms_per_step"],
+            "tflops": total_flops("standard") / (std["ms_per_step"] * 1e-3)
+            / 1e12,
             "gram_speedup": std["ms_per_step"] / ms}
     if not args.no_cpu_baseline:
-        sample = m_cpu if m_cpu.dim() == 2 else m_cpu[0]
+        first = host_inputs[0]
+        sample = first if first.dim() == 2 else first[0]
         cb = cpu_baseline(sample, args.mode, args.restart_mask)
-        if m_cpu.dim() == 3:
-            cb["sample"] += " (one expert of the batch)"
+        if first.dim() == 3 or len(host_inputs) > 1:
+            cb["sample"] += " (one matrix of the set; orth/s per matrix)"
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 

@@ -70,7 +70,8 @@ bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
 // LDS).  For 16-bit products the edge (128, 192 or 256) minimizes a cost
 // estimate of one call: work-group waves over the 256 compute units times
 // the time of one work-group, in units of one 256-edge k-tile, with the
-// per-k-tile and fixed (prologue and epilogue) costs measured on MI355X.
+// per-k-tile and fixed (prologue and epilogue) costs measured on MI355X with
+// random operands.
 // Smaller tiles lose MFMA efficiency (more LDS reads per MFMA) but fill the
 // chip when a product has few tiles.
 struct TileCost {
@@ -78,9 +79,9 @@ struct TileCost {
   double sym_ktile, sym_fixed, nn_ktile, nn_fixed;
 };
 constexpr TileCost kTileCosts[] = {
-    {128, 0.40, 8.0, 0.40, 8.0},
-    {192, 0.55, 13.5, 0.55, 15.0},
-    {256, 1.00, 22.0, 1.00, 24.0},
+    {128, 0.45, 8.0, 0.45, 9.0},
+    {192, 0.67, 13.0, 0.67, 14.0},
+    {256, 1.00, 18.0, 1.00, 20.0},
 };
 constexpr double kComputeUnits = 256.0;
 
@@ -89,7 +90,7 @@ double tile_estimate(const TileCost& c, int64_t n, int64_t m, int64_t batch, ns_
   const double nt = (double)(n_pad / c.edge);
   const double sym_waves = ceil(nt * (nt + 1) / 2 * (double)batch / kComputeUnits);
   const double nn_waves = ceil(nt * (double)(m_pad / tn) * (double)batch / kComputeUnits);
-  const double kn = (double)n_pad / 64, km = (double)m_pad / 64;
+  const double kn = ceil((double)n / 64), km = ceil((double)m / 64);  // contractions stop at the real size
   const double sym = sym_waves * (kn * c.sym_ktile + c.sym_fixed);
   const double gram = sym_waves * (km * c.sym_ktile + c.sym_fixed);
   const double nn = nn_waves * (kn * c.nn_ktile + c.nn_fixed);
