@@ -41,6 +41,9 @@ come from the oracle itself):
 * ``soft_threshold_split``: the closed form of the l1 proximal step, its
   subgradient optimality conditions and Student-t(2) order statistics.
 * ``lower_median_abs``: brute-force sort on small inputs.
+* ``muon_step`` / ``momentum_update``: the momentum recurrence against its
+  geometric-series closed form for a constant gradient, and the whole step
+  against ``W - lr U diag(p^T(s/||s||)) V^T`` on a designed spectrum.
 
 No function here is "parity unpinned".
 """
@@ -49,10 +52,11 @@ from .ns import (CLASSIC_ABC, TUNED_ABC, coefficient_schedule, frobenius_stage,
                  ns_gram, ns_standard, scalar_map)
 from .svd import jacobi_svd, polar_eigh, polar_jacobi, orthogonalization_mse
 from .soft_threshold import lower_median_abs, soft_threshold_split
+from .muon import momentum_update, muon_step
 
 __all__ = [
     "CLASSIC_ABC", "TUNED_ABC", "coefficient_schedule", "frobenius_stage",
     "ns_gram", "ns_standard", "scalar_map", "jacobi_svd", "polar_eigh",
     "polar_jacobi", "orthogonalization_mse", "lower_median_abs",
-    "soft_threshold_split",
+    "soft_threshold_split", "momentum_update", "muon_step",
 ]

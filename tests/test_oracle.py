@@ -14,8 +14,9 @@ import numpy as np
 import pytest
 
 from oracle import (CLASSIC_ABC, TUNED_ABC, jacobi_svd, lower_median_abs,
-                    ns_gram, ns_standard, orthogonalization_mse, polar_eigh,
-                    polar_jacobi, scalar_map, soft_threshold_split)
+                    momentum_update, muon_step, ns_gram, ns_standard,
+                    orthogonalization_mse, polar_eigh, polar_jacobi,
+                    scalar_map, soft_threshold_split)
 import workloads
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -247,3 +248,53 @@ def test_soft_threshold_student_t_statistics():
     assert abs(lam - math.sqrt(6.0)) < 0.01 * math.sqrt(6.0)
     frac = float(np.mean(o != 0))
     assert abs(frac - (1.0 - math.sqrt(3.0) / 2.0)) < 2e-3
+
+
+# ---------------------------------------------------------------------------
+# Muon step: momentum recurrence and the whole update in closed form.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_momentum_constant_gradient_geometric_series(nesterov):
+    # With M_0 = 0 and a constant gradient G, M_t = G (1 - mu^t) / (1 - mu):
+    # the sum of a geometric series, independent of the recurrence's code.
+    rng = np.random.default_rng(0)
+    g = rng.standard_normal((5, 7))
+    mu = 0.95
+    m = np.zeros_like(g)
+    for t in range(1, 13):
+        m, u = momentum_update(m, g, mu, nesterov)
+        geo = (1.0 - mu ** t) / (1.0 - mu)
+        assert np.allclose(m, geo * g, rtol=1e-13, atol=0)
+        expect_u = g * (1.0 + mu * geo) if nesterov else geo * g
+        assert np.allclose(u, expect_u, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_muon_step_designed_spectrum(mode, nesterov):
+    # G = U diag(s) V^T and M = c G: the step's NS input is a multiple of G,
+    # Frobenius normalization removes the multiple, so
+    # W' = W - lr U diag(p^T(s / ||s||)) V^T exactly (eps = 0).
+    s = np.geomspace(1.0, 2e-3, 24)
+    g, u, v = workloads.designed_spectrum(24, 60, s, seed=11)
+    rng = np.random.default_rng(1)
+    w = rng.standard_normal(g.shape)
+    m0 = 0.3 * g
+    lr = 0.02
+    w1, m1 = muon_step(w, g, m0, lr, 0.95, nesterov, mode=mode, eps=0.0)
+    expect_o = (u * scalar_map(s / np.linalg.norm(s))[None, :]) @ v.T
+    assert _rel(w - w1, lr * expect_o) < 1e-12
+    assert np.allclose(m1, 0.95 * m0 + g, rtol=1e-14, atol=1e-15)
+
+
+def test_muon_step_zero_lr_and_inputs_untouched():
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((8, 20))
+    g = rng.standard_normal((8, 20))
+    m = rng.standard_normal((8, 20))
+    copies = (w.copy(), g.copy(), m.copy())
+    w1, m1 = muon_step(w, g, m, 0.0)
+    assert np.array_equal(w1, w)
+    for a, b in zip((w, g, m), copies):
+        assert np.array_equal(a, b)

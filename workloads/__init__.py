@@ -123,9 +123,6 @@ def designed_spectrum(r: int, c: int, s: np.ndarray, seed: int):
 # The five named workloads.
 # ---------------------------------------------------------------------------
 
-TUNED_ABC = (3.4445, -4.7750, 2.0315)
-
-
 def small_fp32(seed: int = 1) -> torch.Tensor:
     """One 256 x 1024 fp32 matrix with i.i.d. N(0, 1) entries."""
     return gaussian((256, 1024), seed, "fp32")
