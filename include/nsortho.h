@@ -64,7 +64,8 @@ typedef enum {
   NS_KERNEL_GRAM = 2,      /* X X^T, inner dimension m (symmetric result) */
   NS_KERNEL_SYM = 3,       /* n x n symmetric products: b A + c A^2, Z' Q, Z' R, Z' V */
   NS_KERNEL_UPDATE = 4,    /* (n x n) X products: a X + B X, Q X */
-  NS_KERNEL_THRESHOLD = 5  /* soft-threshold select and split */
+  NS_KERNEL_THRESHOLD = 5, /* soft-threshold select and split */
+  NS_KERNEL_MOMENTUM = 6   /* Muon momentum update (HBM read + write) */
 } ns_kernel_kind;
 
 /* Optional launch trace, for measuring kernels on the caller's stream.
@@ -191,6 +192,46 @@ ns_status ns_soft_threshold_split(const void* M, void* B, void* O,
                                   float mult, float* d_lambda_out,
                                   void* workspace, size_t workspace_bytes,
                                   ns_stream_t stream);
+
+/*
+ * One Muon optimizer step on `batch` equal-shape weight matrices (batch = 1
+ * for one matrix):
+ *
+ *     M <- momentum * M + G
+ *     U  = G + momentum * M        (nesterov != 0)   or   U = M
+ *     W <- W - lr * NS(U)
+ *
+ * (Gram Newton-Schulz article on itsolotime.com, "Algorithm advantages
+ * ...": Muon's update takes the polar factor of the momentum, with a
+ * momentum coefficient and a learning rate; Muon / NanoGPT article,
+ * "Engineering reproduction checklist": momentum 0.95 with Nesterov, five
+ * Newton-Schulz steps.)  NS(U) is exactly what ns_orthogonalize_batched
+ * computes for U with the same steps, coefficients, mode and options; no
+ * shape-dependent factor is applied to lr.
+ *
+ *   W        device, dtype `dtype`; matrix e at W + e * batch_stride,
+ *            row-major with leading dimension ld; updated in place.
+ *   G        device, same dtype and layout as W; read only.
+ *   M        device fp32 momentum, same layout as W (ld and batch_stride in
+ *            elements); updated in place.
+ *   lr       finite learning rate; momentum in [0, 1).
+ *   workspace   ns_muon_workspace_size(...) bytes, 256-byte aligned.
+ * U is formed in fp32 and rounded to `dtype` before the orthogonalization;
+ * the new W is W + (-lr) * O in fp32 from O rounded to `dtype`, rounded
+ * once more to `dtype`.  d_status (if set) flags non-finite entries of O.
+ * Other arguments and errors as for ns_orthogonalize_batched.
+ */
+size_t ns_muon_workspace_size(int64_t rows, int64_t cols, int64_t batch,
+                              ns_dtype dtype, ns_mode mode,
+                              const ns_options* opt);
+
+ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch,
+                       int64_t rows, int64_t cols, int64_t ld,
+                       int64_t batch_stride, ns_dtype dtype, float lr,
+                       float momentum, int32_t nesterov, int32_t steps,
+                       const float* a, const float* b, const float* c,
+                       ns_mode mode, const ns_options* opt, void* workspace,
+                       size_t workspace_bytes, ns_stream_t stream);
 
 /* Static description of a status code. */
 const char* ns_status_string(ns_status s);

@@ -2,17 +2,20 @@
 
 Python face of ``libnsortho.so``: the standard and Gram forms of quintic
 Newton-Schulz (Muon's approximate polar factor), a batched launcher for
-equal-shape expert matrices and the ROOT soft-threshold split.  The HIP
+equal-shape expert matrices, the ROOT soft-threshold split and a whole Muon
+step (momentum, orthogonalization, weight update).  The HIP
 library does all the work; this package only marshals arguments.
 """
 
 from .flops import gram_flops, ns_flops, standard_flops
-from ._binding import (NS_MAX_STEPS, TUNED_ABC, NSError, lib, orthogonalize,
+from ._binding import (NS_MAX_STEPS, TUNED_ABC, NSError, lib, muon_step,
+                       muon_workspace_size, orthogonalize,
                        orthogonalize_batched, soft_threshold_split,
                        status_string, workspace_size)
 
 __all__ = [
-    "NS_MAX_STEPS", "TUNED_ABC", "NSError", "lib", "orthogonalize",
+    "NS_MAX_STEPS", "TUNED_ABC", "NSError", "lib", "muon_step",
+    "muon_workspace_size", "orthogonalize",
     "orthogonalize_batched", "soft_threshold_split", "status_string",
     "workspace_size", "gram_flops", "ns_flops", "standard_flops",
 ]

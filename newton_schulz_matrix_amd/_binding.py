@@ -61,7 +61,8 @@ class Options(ctypes.Structure):
                 ("tile", ctypes.c_int32)]
 
 
-KERNEL_KINDS = ("norm", "stage", "gram", "sym", "update", "threshold")
+KERNEL_KINDS = ("norm", "stage", "gram", "sym", "update", "threshold",
+                "momentum")
 
 
 _LIB = None
@@ -99,6 +100,20 @@ _SIGNATURES = {
                                  ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                  ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_size_t, ctypes.c_void_p]),
+    "ns_muon_workspace_size": (ctypes.c_size_t,
+                               [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                ctypes.c_int, ctypes.c_int,
+                                ctypes.POINTER(Options)]),
+    "ns_muon_step": (ctypes.c_int,
+                     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                      ctypes.c_float, ctypes.c_float, ctypes.c_int32,
+                      ctypes.c_int32, ctypes.POINTER(ctypes.c_float),
+                      ctypes.POINTER(ctypes.c_float),
+                      ctypes.POINTER(ctypes.c_float), ctypes.c_int,
+                      ctypes.POINTER(Options), ctypes.c_void_p,
+                      ctypes.c_size_t, ctypes.c_void_p]),
     "ns_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ns_version": (ctypes.c_int32, []),
 }
@@ -268,6 +283,64 @@ def orthogonalize_batched(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
         ctypes.c_void_p(wptr), wbytes, _stream_handle(x.device))
     _check(st, "ns_orthogonalize_batched")
     return x
+
+
+def muon_step(w: torch.Tensor, g: torch.Tensor, m: torch.Tensor, lr: float,
+              momentum: float = 0.95, nesterov: bool = True, steps: int = 5,
+              abc=TUNED_ABC, mode: str = "gram", restart_mask: int = 1 << 4,
+              eps: float = 1e-7, internal: Optional[str] = None,
+              status: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None,
+              trace: Optional[Trace] = None, tile: int = 0) -> torch.Tensor:
+    """One Muon step, in place: M <- mu M + G; W <- W - lr NS(G + mu M).
+
+    ``w`` and ``g``: [rows, cols] or [E, rows, cols] device tensors of the
+    same dtype and strides (rows contiguous); ``m``: fp32 momentum with the
+    same shape and strides.  ``nesterov=False`` orthogonalizes M itself.
+    Returns ``w``.
+    """
+    if w.shape != g.shape or w.shape != m.shape:
+        raise ValueError("w, g and m must have the same shape")
+    if w.dtype != g.dtype or m.dtype != torch.float32:
+        raise TypeError("g must have w's dtype and m must be float32")
+    if w.stride() != g.stride() or w.stride() != m.stride():
+        raise ValueError("w, g and m must have the same strides")
+    batched = w.dim() == 3
+    _check_matrix(w, 3 if batched else 2)
+    if not (g.is_cuda and m.is_cuda):
+        raise ValueError("expects device tensors")
+    batch = w.shape[0] if batched else 1
+    rows, cols = w.shape[-2], w.shape[-1]
+    ld = w.stride(-2) if rows > 1 else cols
+    bstride = w.stride(0) if batched and batch > 1 else rows * ld
+    code = dtype_code(w.dtype)
+    opt = make_options(restart_mask, eps, internal, status, trace, tile)
+    need = int(lib().ns_muon_workspace_size(rows, cols, batch, code,
+                                            _MODE_CODE[mode],
+                                            ctypes.byref(opt)))
+    if need == 0:
+        raise NSError(1, "ns_muon_workspace_size")
+    wptr, wbytes, keep = _workspace(need, w.device, workspace)
+    a, b, c = _coefficients(abc, steps)
+    st = lib().ns_muon_step(
+        ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+        ctypes.c_void_p(m.data_ptr()), batch, rows, cols, ld, bstride, code,
+        float(lr), float(momentum), 1 if nesterov else 0, steps, a, b, c,
+        _MODE_CODE[mode], ctypes.byref(opt), ctypes.c_void_p(wptr), wbytes,
+        _stream_handle(w.device))
+    _check(st, "ns_muon_step")
+    return w
+
+
+def muon_workspace_size(rows: int, cols: int, batch: int = 1,
+                        dtype: torch.dtype = torch.bfloat16,
+                        mode: str = "gram", restart_mask: int = 1 << 4,
+                        internal: Optional[str] = None, tile: int = 0) -> int:
+    opt = make_options(restart_mask, 1e-7, internal, tile=tile)
+    return int(lib().ns_muon_workspace_size(rows, cols, batch,
+                                            dtype_code(dtype),
+                                            _MODE_CODE[mode],
+                                            ctypes.byref(opt)))
 
 
 def soft_threshold_split(m: torch.Tensor, lam: Optional[float] = None,

@@ -212,8 +212,12 @@ struct Runner {
   const Plan& p;
   char* ws;
   hipStream_t st;
-  IO* user;
+  IO* user;                  // input, read by the norm and staging passes
   int64_t ld, bstride;
+  IO* out;                   // written by the final epilogue
+  int64_t out_ld, out_bstride;
+  bool accumulate;           // false: out = result; true: out += apply * result
+  float apply;
   const ns_options* opt;
   Tracer tr;
 
@@ -290,6 +294,8 @@ struct Runner {
     a.m_real = (int)p.m;
     a.transpose_out = 0;
     a.final_out = 0;
+    a.accumulate = 0;
+    a.apply_scale = 0.f;
     a.alpha = alpha;
     a.gamma = 1.f;
     a.out_scale = 1.f;
@@ -307,18 +313,20 @@ struct Runner {
     a.B = B;
     a.XT = xtbuf(xin);
     a.E = with_e ? xbuf(xin) : nullptr;
-    a.Y = user;
+    a.Y = out;
     a.YT = nullptr;
     a.sB = p.nn_elems;
     a.sXT = p.x_elems;
     a.sE = p.x_elems;
-    a.sY = bstride;
+    a.sY = out_bstride;
     a.sYT = 0;
     a.ldb = (int)p.n_pad;
     a.ldxt = (int)p.n_pad;
     a.lde = (int)p.m_pad;
     a.ldyt = 0;
-    a.ldy = ld;
+    a.ldy = out_ld;
+    a.accumulate = accumulate ? 1 : 0;
+    a.apply_scale = apply;
     a.K = (int)k_extent(p.n);
     a.tiles_m = (int)(p.n_pad / TILE);
     a.tiles_n = (int)(p.m_pad / nn_tile_n(TILE));
@@ -426,10 +434,31 @@ struct Runner {
   }
 };
 
+// Where a call reads its input and writes its result.
+struct IoSpec {
+  void* in;
+  int64_t ld, bstride;
+  void* out;
+  int64_t out_ld, out_bstride;
+  bool accumulate;  // false: out = result; true: out += apply * result
+  float apply;
+};
+
 template <typename T, typename IO>
-ns_status run_typed(const Plan& p, void* X, int64_t ld, int64_t bstride, int steps, const float* a, const float* b,
-                    const float* c, const ns_options* opt, void* ws, hipStream_t st) {
-  Runner<T, IO> r{p, reinterpret_cast<char*>(ws), st, reinterpret_cast<IO*>(X), ld, bstride, opt,
+ns_status run_typed(const Plan& p, const IoSpec& io, int steps, const float* a, const float* b, const float* c,
+                    const ns_options* opt, void* ws, hipStream_t st) {
+  Runner<T, IO> r{p,
+                  reinterpret_cast<char*>(ws),
+                  st,
+                  reinterpret_cast<IO*>(io.in),
+                  io.ld,
+                  io.bstride,
+                  reinterpret_cast<IO*>(io.out),
+                  io.out_ld,
+                  io.out_bstride,
+                  io.accumulate,
+                  io.apply,
+                  opt,
                   Tracer{opt ? opt->trace : nullptr, st}};
   const float eps = opt ? opt->eps : 1e-7f;
   hipError_t e;
@@ -444,6 +473,32 @@ ns_status run_typed(const Plan& p, void* X, int64_t ld, int64_t bstride, int ste
   }
   return hip_status(e);
 }
+
+// Calls f.template run<T, IO>() for the (internal, I/O) type pair of a plan.
+template <class F>
+ns_status dispatch_types(const Plan& p, F&& f) {
+  if (p.io == NS_FP32) return f.template run<float, float>();
+  if (p.io == NS_BF16) {
+    if (p.internal == NS_FP16) return f.template run<_Float16, __bf16>();
+    return f.template run<__bf16, __bf16>();
+  }
+  if (p.internal == NS_FP16) return f.template run<_Float16, _Float16>();
+  return f.template run<__bf16, _Float16>();
+}
+
+struct OrthCall {
+  const Plan& p;
+  IoSpec io;
+  int32_t steps;
+  const float *a, *b, *c;
+  const ns_options* opt;
+  void* ws;
+  hipStream_t st;
+  template <typename T, typename IO>
+  ns_status run() const {
+    return run_typed<T, IO>(p, io, steps, a, b, c, opt, ws, st);
+  }
+};
 
 ns_status check_coefficients(int32_t steps, const float* a, const float* b, const float* c, ns_mode mode,
                              uint32_t mask, ns_dtype internal) {
@@ -476,14 +531,69 @@ ns_status orthogonalize_impl(void* X, int64_t batch, int64_t rows, int64_t cols,
   const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
   if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal)) != NS_OK) return s;
   if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == NS_FP32) return run_typed<float, float>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
-  if (dtype == NS_BF16) {
-    if (p.internal == NS_FP16) return run_typed<_Float16, __bf16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
-    return run_typed<__bf16, __bf16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
+  return dispatch_types(p, OrthCall{p, IoSpec{X, ld, bstride, X, ld, bstride, false, 0.f}, steps, a, b, c, opt, ws,
+                                    reinterpret_cast<hipStream_t>(stream)});
+}
+
+// Muon step: the momentum pass writes U into the workspace after the
+// orthogonalization's own buffers; the orthogonalization then reads U and
+// its final epilogue applies W <- W - lr * NS(U).
+size_t muon_u_offset(const Plan& p) { return align_up(p.total); }
+size_t muon_total(const Plan& p) {
+  return muon_u_offset(p) + align_up((size_t)p.batch * p.rows * p.cols * elem_size(p.io));
+}
+
+// The Muon step for one (internal, I/O) type pair: momentum pass, then the
+// orthogonalization of U with W <- W - lr * result in its final epilogue.
+struct MuonCall {
+  const Plan& p;
+  void *W, *U;
+  const void* G;
+  float* M;
+  int64_t ld, bstride;
+  float lr, mu;
+  int32_t nesterov, steps;
+  const float *a, *b, *c;
+  const ns_options* opt;
+  void* ws;
+  hipStream_t st;
+  template <typename T, typename IO>
+  ns_status run() const {
+    const int v = 16 / (int)sizeof(IO);
+    const bool vec_ok = ld % v == 0 && (p.batch == 1 || bstride % v == 0) &&
+                        (reinterpret_cast<uintptr_t>(G) & 15) == 0 && (reinterpret_cast<uintptr_t>(M) & 15) == 0;
+    const double elems = (double)p.rows * (double)p.cols * (double)p.batch;
+    Tracer tr{opt ? opt->trace : nullptr, st};
+    hipError_t e = tr.run(NS_KERNEL_MOMENTUM, 0.0, elems * (2.0 * sizeof(IO) + 8.0), [&] {
+      hipLaunchKernelGGL((k_momentum<IO>), dim3((unsigned)p.rows, (unsigned)p.batch), dim3(kStageThreads), 0, st,
+                         reinterpret_cast<const IO*>(G), M, reinterpret_cast<IO*>(U), p.cols, ld, bstride,
+                         vec_ok ? 1 : 0, mu, nesterov ? 1 : 0);
+      return hipGetLastError();
+    });
+    if (e != hipSuccess) return NS_ERR_HIP;
+    return run_typed<T, IO>(p, IoSpec{U, p.cols, p.rows * p.cols, W, ld, bstride, true, -lr}, steps, a, b, c, opt, ws,
+                            st);
   }
-  if (p.internal == NS_FP16) return run_typed<_Float16, _Float16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
-  return run_typed<__bf16, _Float16>(p, X, ld, bstride, steps, a, b, c, opt, ws, st);
+};
+
+ns_status muon_impl(void* W, const void* G, float* M, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                    int64_t bstride, ns_dtype dtype, float lr, float mu, int32_t nesterov, int32_t steps,
+                    const float* a, const float* b, const float* c, ns_mode mode, const ns_options* opt, void* ws,
+                    size_t ws_bytes, ns_stream_t stream) {
+  if (!W || !G || !M) return NS_ERR_INVALID_ARG;
+  if (ld < cols) return NS_ERR_INVALID_ARG;
+  if (batch > 1 && bstride < rows * ld) return NS_ERR_INVALID_ARG;
+  if (!isfinite(lr) || !(mu >= 0.f && mu < 1.f)) return NS_ERR_INVALID_ARG;
+  Plan p;
+  ns_status s = make_plan(rows, cols, batch, dtype, mode, opt, &p);
+  if (s != NS_OK) return s;
+  if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
+  const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
+  if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal)) != NS_OK) return s;
+  if (!ws || ws_bytes < muon_total(p) || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
+  void* U = reinterpret_cast<char*>(ws) + muon_u_offset(p);
+  return dispatch_types(p, MuonCall{p, W, U, G, M, ld, bstride, lr, mu, nesterov, steps, a, b, c, opt, ws,
+                                    reinterpret_cast<hipStream_t>(stream)});
 }
 
 // Soft-threshold workspace: select state + three histograms.
@@ -566,6 +676,21 @@ ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows, int64_t
                             workspace_bytes, stream);
 }
 
+size_t ns_muon_workspace_size(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode,
+                              const ns_options* opt) {
+  Plan p;
+  if (make_plan(rows, cols, batch, dtype, mode, opt, &p) != NS_OK) return 0;
+  return muon_total(p);
+}
+
+ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
+                       int64_t batch_stride, ns_dtype dtype, float lr, float momentum, int32_t nesterov,
+                       int32_t steps, const float* a, const float* b, const float* c, ns_mode mode,
+                       const ns_options* opt, void* workspace, size_t workspace_bytes, ns_stream_t stream) {
+  return muon_impl(W, G, M, batch, rows, cols, ld, batch == 1 ? rows * ld : batch_stride, dtype, lr, momentum,
+                   nesterov, steps, a, b, c, mode, opt, workspace, workspace_bytes, stream);
+}
+
 size_t ns_soft_threshold_workspace_size(int64_t numel, ns_dtype dtype) {
   if (numel < 1) return 0;
   if (dtype != NS_BF16 && dtype != NS_FP16 && dtype != NS_FP32) return 0;
@@ -597,6 +722,6 @@ const char* ns_status_string(ns_status s) {
   return "unknown status";
 }
 
-int32_t ns_version(void) { return 100; }
+int32_t ns_version(void) { return 200; }
 
 }  // extern "C"

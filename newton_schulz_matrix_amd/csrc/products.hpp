@@ -475,8 +475,29 @@ struct NTArgs {
   int transpose_out;   // final output: write element (i, j) to Y[j * ldy + i]
   int final_out;       // 1: bounds-checked store in OutT with out_scale
   float alpha, gamma, out_scale;
+  int accumulate;      // final output only: 0 stores the result; 1: Y <- Y + apply_scale * result
+  float apply_scale;
   int32_t* d_status;
 };
+
+// The caller's 16-byte chunk `dst` gets `val` (kEC rounded results), or
+// with `acc`, dst + s * val computed in fp32 and rounded once more.
+template <typename OutT>
+__device__ __forceinline__ void final_chunk(OutT* dst, uint4 val, int acc, float s) {
+  if (acc) {
+    constexpr int kEC = 16 / (int)sizeof(OutT);
+    const uint4 old = *reinterpret_cast<const uint4*>(dst);
+    const OutT* o = reinterpret_cast<const OutT*>(&old);
+    OutT* v = reinterpret_cast<OutT*>(&val);
+#pragma unroll
+    for (int e = 0; e < kEC; ++e) v[e] = from_f32<OutT>(fmaf(s, to_f32<OutT>(v[e]), to_f32<OutT>(o[e])));
+  }
+  *reinterpret_cast<uint4*>(dst) = val;
+}
+template <typename OutT>
+__device__ __forceinline__ void final_elem(OutT* dst, OutT val, int acc, float s) {
+  *dst = acc ? from_f32<OutT>(fmaf(s, to_f32<OutT>(val), to_f32<OutT>(*dst))) : val;
+}
 
 // Work-groups are dealt to the 8 XCDs round-robin (work-group b runs on XCD
 // b % 8), and each XCD has its own L2.  xcd_order(b, count) returns the
@@ -796,10 +817,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
       const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
       OutT* dst = Y + i * p.ldy + j0;
       if (vec && j0 + kEC <= p.m_real) {
-        *reinterpret_cast<uint4*>(dst) = val;
+        final_chunk(dst, val, p.accumulate, p.apply_scale);
       } else {
         const OutT* vals = reinterpret_cast<const OutT*>(&val);
-        for (int e = 0; e < kEC && j0 + e < p.m_real; ++e) dst[e] = vals[e];
+        for (int e = 0; e < kEC && j0 + e < p.m_real; ++e) final_elem(dst + e, vals[e], p.accumulate, p.apply_scale);
       }
     }
   } else {
@@ -813,10 +834,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
       const uint4 val = TL::column_chunk(c * kEC, jj);
       OutT* dst = Y + j * p.ldy + i0;
       if (vec && i0 + kEC <= p.n_real) {
-        *reinterpret_cast<uint4*>(dst) = val;
+        final_chunk(dst, val, p.accumulate, p.apply_scale);
       } else {
         const OutT* vals = reinterpret_cast<const OutT*>(&val);
-        for (int e = 0; e < kEC && i0 + e < p.n_real; ++e) dst[e] = vals[e];
+        for (int e = 0; e < kEC && i0 + e < p.n_real; ++e) final_elem(dst + e, vals[e], p.accumulate, p.apply_scale);
       }
     }
   }

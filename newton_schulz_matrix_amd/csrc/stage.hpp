@@ -161,6 +161,66 @@ __global__ void __launch_bounds__(kStageThreads) k_stage_pair(const IO* M, int64
   }
 }
 
+// Muon momentum: M <- mu M + G (fp32), U = G + mu M (Nesterov) or M, U
+// rounded to IO and stored contiguously (rows x cols per matrix).  One
+// block per row; 8 consecutive elements per thread, vectorized when rows
+// are 16-byte aligned.
+template <typename IO>
+__global__ void __launch_bounds__(kStageThreads) k_momentum(const IO* G, float* M, IO* U, int64_t cols, int64_t ld,
+                                                           int64_t bstride, int vec_ok, float mu, int nesterov) {
+  constexpr int kV = 8;
+  const int64_t b = blockIdx.y, i = blockIdx.x;
+  const IO* g = G + b * bstride + i * ld;
+  float* m = M + b * bstride + i * ld;
+  IO* u = U + (b * (int64_t)gridDim.x + i) * cols;
+  for (int64_t c0 = (int64_t)threadIdx.x * kV; c0 < cols; c0 += (int64_t)kStageThreads * kV) {
+    float gv[kV], mv[kV];
+    const bool full = vec_ok && c0 + kV <= cols;
+    if (full) {
+      IO e[kV];
+      if constexpr (sizeof(IO) == 2) {
+        *reinterpret_cast<uint4*>(e) = *reinterpret_cast<const uint4*>(g + c0);
+      } else {
+        reinterpret_cast<uint4*>(e)[0] = reinterpret_cast<const uint4*>(g + c0)[0];
+        reinterpret_cast<uint4*>(e)[1] = reinterpret_cast<const uint4*>(g + c0)[1];
+      }
+#pragma unroll
+      for (int k = 0; k < kV; ++k) gv[k] = to_f32<IO>(e[k]);
+      *reinterpret_cast<float4*>(mv) = reinterpret_cast<const float4*>(m + c0)[0];
+      *reinterpret_cast<float4*>(mv + 4) = reinterpret_cast<const float4*>(m + c0)[1];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kV; ++k) {
+        gv[k] = c0 + k < cols ? to_f32<IO>(g[c0 + k]) : 0.f;
+        mv[k] = c0 + k < cols ? m[c0 + k] : 0.f;
+      }
+    }
+    IO uo[kV];
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      mv[k] = fmaf(mu, mv[k], gv[k]);
+      uo[k] = from_f32<IO>(nesterov ? fmaf(mu, mv[k], gv[k]) : mv[k]);
+    }
+    if (full) {
+      reinterpret_cast<float4*>(m + c0)[0] = *reinterpret_cast<const float4*>(mv);
+      reinterpret_cast<float4*>(m + c0)[1] = *reinterpret_cast<const float4*>(mv + 4);
+    } else {
+      for (int k = 0; k < kV && c0 + k < cols; ++k) m[c0 + k] = mv[k];
+    }
+    // U rows are contiguous: 16-byte stores when the row start is aligned.
+    if (full && ((cols * (int64_t)sizeof(IO)) % 16 == 0)) {
+      if constexpr (sizeof(IO) == 2) {
+        *reinterpret_cast<uint4*>(u + c0) = *reinterpret_cast<const uint4*>(uo);
+      } else {
+        reinterpret_cast<uint4*>(u + c0)[0] = reinterpret_cast<const uint4*>(uo)[0];
+        reinterpret_cast<uint4*>(u + c0)[1] = reinterpret_cast<const uint4*>(uo)[1];
+      }
+    } else {
+      for (int k = 0; k < kV && c0 + k < cols; ++k) u[c0 + k] = uo[k];
+    }
+  }
+}
+
 // Fill n x n (ld) blocks of a batch with zero (used to clear buffers
 // without memset nodes, so that the sequence can be captured in a graph).
 template <typename T>

@@ -32,6 +32,7 @@ def _declared_functions():
 def test_header_declares_the_api():
     names = _declared_functions()
     for want in ["ns_orthogonalize", "ns_orthogonalize_batched",
+                 "ns_muon_step", "ns_muon_workspace_size",
                  "ns_soft_threshold_split", "ns_workspace_size",
                  "ns_soft_threshold_workspace_size", "ns_status_string",
                  "ns_options_default", "ns_version"]:
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.ns_version() >= 100
+    assert lib.ns_version() >= 200
 
 
 def test_status_strings():
@@ -196,3 +197,37 @@ def test_soft_threshold_argument_checks():
     assert call(dt=4) == 2
     assert call(wsb=need - 1) == 3
     assert call(ws=0) == 3
+
+
+def test_muon_workspace_and_argument_checks():
+    lib = B.lib()
+    # The Muon workspace is the orthogonalization's plus one U buffer in the
+    # I/O dtype.
+    ns_ws = nsa.workspace_size(300, 700, 2, torch.bfloat16, "gram")
+    mu_ws = nsa.muon_workspace_size(300, 700, 2, torch.bfloat16, "gram")
+    assert ns_ws + 2 * 300 * 700 * 2 <= mu_ws <= ns_ws + 2 * 300 * 700 * 2 + 512
+    assert lib.ns_muon_workspace_size(0, 5, 1, 0, 1, None) == 0
+    a, b, c = B._coefficients(B.TUNED_ABC, 5)
+    need = lib.ns_muon_workspace_size(8, 8, 1, B.NS_BF16, B.NS_GRAM, None)
+
+    def call(W=256, G=256, M=256, batch=1, rows=8, cols=8, ld=8, bs=64,
+             dt=B.NS_BF16, lr=0.02, mom=0.95, nest=1, steps=5, mode=B.NS_GRAM,
+             ws=256, wsb=None):
+        return lib.ns_muon_step(
+            ctypes.c_void_p(W), ctypes.c_void_p(G), ctypes.c_void_p(M), batch,
+            rows, cols, ld, bs, dt, lr, mom, nest, steps, a, b, c, mode, None,
+            ctypes.c_void_p(ws), need if wsb is None else wsb, None)
+    inv, dt, wsp = 1, 2, 3
+    assert call(W=0) == inv
+    assert call(G=0) == inv
+    assert call(M=0) == inv
+    assert call(ld=7) == inv
+    assert call(batch=2, bs=32) == inv          # stride below one matrix
+    assert call(lr=float("nan")) == inv
+    assert call(lr=float("inf")) == inv
+    assert call(mom=1.0) == inv
+    assert call(mom=-0.1) == inv
+    assert call(steps=0) == inv
+    assert call(dt=7) == dt
+    assert call(wsb=need - 1) == wsp
+    assert call(ws=0) == wsp
