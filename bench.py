@@ -12,7 +12,9 @@ Other workloads (--workload): the transposed and square Llama shapes, the
 MoE expert batch (128 x 2048 x 1408 and transposed), the NanoGPT-124M
 weight set (three batched calls per step), the ROOT split of a 2048 x 8192
 Student-t gradient followed by orthogonalization of its robust part, and a
-256 x 1024 fp32 matrix.  `value` counts matrices per second.
+256 x 1024 fp32 matrix, and a whole Muon step (momentum, orthogonalization,
+weight update) with the 4096 x 14336 matrix as the gradient.  `value`
+counts matrices per second.
 
 Prints one JSON line.  Besides the driver's fields it carries:
   tflops / mfma_frac     algorithmic (symmetric-aware) TFLOP/s of the whole
@@ -58,7 +60,7 @@ def parse():
     ap.add_argument("--workload", default="llama8b-mlp",
                     choices=["llama8b-mlp", "llama8b-down", "llama8b-square",
                              "moe-experts", "moe-experts-t", "small-fp32",
-                             "nanogpt-set", "root-split",
+                             "nanogpt-set", "root-split", "muon-step",
                              "copy-calibration"])
     ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
     ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
@@ -72,30 +74,34 @@ def parse():
 
 
 def workload_input(name):
-    """(list of host input tensors, I/O dtype name, ROOT split first?).
+    """(list of host input tensors, I/O dtype name, step kind).
 
-    A 3-D tensor is one batched call; a list of several tensors is run as
-    one call each, in order, per step.
+    The kind is "ns" (orthogonalize each input), "root" (ROOT split, then
+    orthogonalize the robust part) or "muon" (a whole Muon step with the
+    input as the gradient).  A 3-D tensor is one batched call; a list of
+    several tensors is run as one call each, in order, per step.
     """
     import workloads
     if name == "llama8b-mlp":
-        return [workloads.llama8b((4096, 14336))], "bf16", False
+        return [workloads.llama8b((4096, 14336))], "bf16", "ns"
     if name == "llama8b-down":
-        return [workloads.llama8b((14336, 4096))], "bf16", False
+        return [workloads.llama8b((14336, 4096))], "bf16", "ns"
     if name == "llama8b-square":
-        return [workloads.llama8b((4096, 4096))], "bf16", False
+        return [workloads.llama8b((4096, 4096))], "bf16", "ns"
     if name == "moe-experts":
-        return [workloads.moe_experts(128, 2048, 1408)], "bf16", False
+        return [workloads.moe_experts(128, 2048, 1408)], "bf16", "ns"
     if name == "moe-experts-t":
-        return [workloads.moe_experts(128, 1408, 2048)], "bf16", False
+        return [workloads.moe_experts(128, 1408, 2048)], "bf16", "ns"
     if name == "small-fp32":
-        return [workloads.small_fp32()], "fp32", False
+        return [workloads.small_fp32()], "fp32", "ns"
     if name == "nanogpt-set":
         import torch
         groups = workloads.nanogpt_set()
-        return [torch.stack(g) for g in groups.values()], "bf16", False
+        return [torch.stack(g) for g in groups.values()], "bf16", "ns"
     if name == "root-split":
-        return [workloads.heavy_tailed()], "bf16", True
+        return [workloads.heavy_tailed()], "bf16", "root"
+    if name == "muon-step":
+        return [workloads.llama8b((4096, 14336))], "bf16", "muon"
     raise ValueError(name)
 
 
@@ -160,7 +166,7 @@ def trace_stats(events, t):
     return stats
 
 
-def make_step(inputs, mode, args, split):
+def make_step(inputs, mode, args, kind):
     """A closure running one step: every input once (after the split)."""
     import torch
     import newton_schulz_matrix_amd as nsa
@@ -169,33 +175,42 @@ def make_step(inputs, mode, args, split):
         batched = x.dim() == 3
         fn = nsa.orthogonalize_batched if batched else nsa.orthogonalize
         rows, cols = x.shape[-2], x.shape[-1]
-        ws = torch.empty(nsa.workspace_size(rows, cols, x.shape[0] if batched
-                                            else 1, x.dtype, mode,
-                                            args.restart_mask, args.internal,
-                                            args.tile)
+        nb = x.shape[0] if batched else 1
+        size = (nsa.muon_workspace_size if kind == "muon" else
+                nsa.workspace_size)
+        ws = torch.empty(size(rows, cols, nb, x.dtype, mode,
+                              args.restart_mask, args.internal, args.tile)
                          + 256, dtype=torch.uint8, device=x.device)
         kw = dict(mode=mode, restart_mask=args.restart_mask,
                   internal=args.internal, workspace=ws, tile=args.tile)
-        # The ROOT split reads the original gradient and writes B into the
-        # buffer the orthogonalization then works on in place.
-        src = x.clone() if split else None
-        calls.append((fn, x, kw, src))
+        extra = None
+        if kind == "root":
+            # The ROOT split reads the original gradient and writes B into
+            # the buffer the orthogonalization then works on in place.
+            extra = x.clone()
+        elif kind == "muon":
+            # x is the gradient; a zero weight and momentum to update.
+            extra = (torch.zeros_like(x),
+                     torch.zeros(x.shape, dtype=torch.float32, device=x.device))
+        calls.append((fn, x, kw, extra))
 
     def step(trace=None):
-        for fn, x, kw, src in calls:
-            if src is not None:
-                nsa.soft_threshold_split(src, out_b=x)
-            if trace is None:
-                fn(x, **kw)
-            else:
-                fn(x, trace=trace, **kw)
+        for fn, x, kw, extra in calls:
+            tkw = dict(kw) if trace is None else dict(kw, trace=trace)
+            if kind == "muon":
+                w, m = extra
+                nsa.muon_step(w, x, m, 0.02, 0.95, True, **tkw)
+                continue
+            if kind == "root":
+                nsa.soft_threshold_split(extra, out_b=x)
+            fn(x, **tkw)
     return step
 
 
-def run_form(inputs, mode, steps, warmup, args, split=False, trace_kinds=None):
+def run_form(inputs, mode, steps, warmup, args, kind="ns", trace_kinds=None):
     """Warm up, then time `steps` steps; optionally trace some kernel kinds."""
     import torch
-    step = make_step(inputs, mode, args, split)
+    step = make_step(inputs, mode, args, kind)
     # One untraced step first: the first launch of each kernel also loads
     # its code object.  Then warm-up steps with every kind traced, to find
     # the dominant kernel.
@@ -343,7 +358,7 @@ def main():
     from newton_schulz_matrix_amd.flops import ns_flops
 
     dev = torch.device("cuda:0")
-    host_inputs, io, split = workload_input(args.workload)
+    host_inputs, io, kind = workload_input(args.workload)
     inputs = [m.to(dev) for m in host_inputs]
     shapes = [(m.shape[0] if m.dim() == 3 else 1, m.shape[-2], m.shape[-1])
               for m in host_inputs]
@@ -355,7 +370,7 @@ def main():
         return sum(b * ns_flops(r, c, 5, mode, args.restart_mask)
                    for b, r, c in shapes)
 
-    res = run_form(inputs, args.mode, args.steps, args.warmup, args, split)
+    res = run_form(inputs, args.mode, args.steps, args.warmup, args, kind)
     ms = res["ms_per_step"]
     flops = total_flops(args.mode)
     value = matrices * 1000.0 / ms
@@ -411,7 +426,7 @@ def main():
                    "shapes": [f"{b}x{r}x{c}" for b, r, c in shapes],
                    "rows": shapes[0][1], "cols": shapes[0][2],
                    "batch": matrices, "io_dtype": io, "mode": args.mode,
-                   "root_split": split,
+                   "step": kind,
                    "ns_steps": 5, "abc": list(nsa.TUNED_ABC),
                    "restart_mask": args.restart_mask,
                    "tile": args.tile or "auto",
@@ -423,7 +438,7 @@ def main():
     }
     if not args.no_standard and args.mode == "gram":
         std = run_form(inputs, "standard", max(args.steps // 2, 3), 2, args,
-                       split)
+                       kind)
         out["standard_form"] = {
             "ms_per_step": std["ms_per_step"],
             "orth_per_s": matrices * 1000.0 / std["ms_per_step"],
