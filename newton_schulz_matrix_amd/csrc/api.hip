@@ -84,16 +84,33 @@ constexpr TileCost kTileCosts[] = {
     {256, 1.00, 18.0, 1.00, 20.0},
 };
 constexpr double kComputeUnits = 256.0;
+// Launches of short contractions with more tiles than CUs run persistent
+// (see launch_sym); measured, that cuts their per-tile fixed cost to about
+// this fraction.
+constexpr double kPersistentFixed = 0.6;
+
+// True when a product with `tiles` tiles (all matrices) and `ktiles` k-tiles
+// per tile runs as a persistent grid.
+constexpr int kPersistentGroups = 256;
+constexpr int kPersistentMaxKtiles = 48;
+bool use_persistent(int edge, int64_t tiles, int64_t ktiles) {
+  return edge <= 192 && tiles > kPersistentGroups && ktiles <= kPersistentMaxKtiles;
+}
+
+double product_estimate(int edge, double tiles, double ktiles, double per_ktile, double fixed) {
+  const double waves = ceil(tiles / kComputeUnits);
+  if (use_persistent(edge, (int64_t)tiles, (int64_t)ktiles)) fixed *= kPersistentFixed;
+  return waves * (ktiles * per_ktile + fixed);
+}
 
 double tile_estimate(const TileCost& c, int64_t n, int64_t m, int64_t batch, ns_mode mode) {
   const int64_t n_pad = round_up(n, c.edge), tn = nn_tile_n(c.edge), m_pad = round_up(m, tn);
-  const double nt = (double)(n_pad / c.edge);
-  const double sym_waves = ceil(nt * (nt + 1) / 2 * (double)batch / kComputeUnits);
-  const double nn_waves = ceil(nt * (double)(m_pad / tn) * (double)batch / kComputeUnits);
+  const double nt = (double)(n_pad / c.edge), b = (double)batch;
+  const double sym_tiles = nt * (nt + 1) / 2 * b, nn_tiles = nt * (double)(m_pad / tn) * b;
   const double kn = ceil((double)n / 64), km = ceil((double)m / 64);  // contractions stop at the real size
-  const double sym = sym_waves * (kn * c.sym_ktile + c.sym_fixed);
-  const double gram = sym_waves * (km * c.sym_ktile + c.sym_fixed);
-  const double nn = nn_waves * (kn * c.nn_ktile + c.nn_fixed);
+  const double sym = product_estimate(c.edge, sym_tiles, kn, c.sym_ktile, c.sym_fixed);
+  const double gram = product_estimate(c.edge, sym_tiles, km, c.sym_ktile, c.sym_fixed);
+  const double nn = product_estimate(c.edge, nn_tiles, kn, c.nn_ktile, c.nn_fixed);
   // Launch counts of five steps: standard 5 X X^T, 5 n x n, 5 updates; Gram
   // (one restart) 2 X X^T, about 14 n x n products and 2 updates.
   return mode == NS_GRAM ? 2 * gram + 14 * sym + 2 * nn : 5 * (gram + sym + nn);
@@ -192,17 +209,40 @@ struct Tracer {
 // ---------------------------------------------------------------------------
 // Kernel launchers.
 // ---------------------------------------------------------------------------
+// A launch with more tiles than compute units and a short contraction (at
+// most kPersistentMaxKtiles k-tiles, where start-up and epilogue weigh most)
+// runs as a persistent grid of kPersistentGroups work-groups (one per CU of
+// MI355X) that loop over the tiles, so one tile's stores drain while the
+// next one starts; other launches get one work-group per tile.  The 256 tile
+// has no persistent kernel (its registers are full).  Correctness does not
+// depend on the CU count.
 template <typename T, int TILE, bool GRAM_INPUT>
-hipError_t launch_sym(const SymArgs<T>& a, int64_t batch, hipStream_t s) {
-  const int ntri = a.tiles * (a.tiles + 1) / 2;
-  hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT>), dim3(ntri, (unsigned)batch), dim3(kThreads), 0, s, a);
+hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s) {
+  const int64_t ntri = (int64_t)a.tiles * (a.tiles + 1) / 2;
+  a.batch = (int)batch;
+  if constexpr (TILE <= 192) {
+    if (use_persistent(TILE, ntri * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
+      hipLaunchKernelGGL((k_sym_loop<T, TILE, GRAM_INPUT>), dim3(kPersistentGroups), dim3(kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT>), dim3((unsigned)ntri, (unsigned)batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename T, typename OutT, int TILE>
-hipError_t launch_nt(const NTArgs<T, OutT>& a, int64_t batch, hipStream_t s) {
-  const dim3 grid(a.tiles_m * a.tiles_n, (unsigned)batch);
-  hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE)>), grid, dim3(kThreads), 0, s, a);
+hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s) {
+  const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
+  a.batch = (int)batch;
+  if constexpr (TILE <= 192) {
+    if (use_persistent(TILE, per * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
+      hipLaunchKernelGGL((k_nt_loop<T, OutT, TILE, nn_tile_n(TILE)>), dim3(kPersistentGroups), dim3(kThreads), 0,
+                         s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE)>), dim3((unsigned)per, (unsigned)batch), dim3(kThreads),
+                     0, s, a);
   return hipGetLastError();
 }
 

@@ -455,6 +455,7 @@ struct SymArgs {
   int K;             // multiple of the k-tile
   int tiles;         // n / tile edge
   int n_real;
+  int batch;         // matrices (read by the persistent kernel)
   float alpha_unused;
   float beta, gamma, delta;
 };
@@ -471,6 +472,7 @@ struct NTArgs {
   int64_t ldy;
   int K;             // = n padded
   int tiles_m, tiles_n;
+  int batch;         // matrices (read by the persistent kernel)
   int n_real, m_real;  // valid output rows/cols (wide orientation)
   int transpose_out;   // final output: write element (i, j) to Y[j * ldy + i]
   int final_out;       // 1: bounds-checked store in OutT with out_scale
@@ -625,17 +627,12 @@ struct EPrefetch {
   }
 };
 
-// GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
-// n x n products into their own kernel symbol, so profiles list them apart.
-template <typename T, int TILE, bool GRAM_INPUT>
-__global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
+// One upper-triangle tile (tm <= tn) of matrix bz of a symmetric product.
+template <typename T, int TILE>
+__device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, int bz) {
   using A = Acc<T, TILE, TILE>;
   constexpr int FM = A::FM, FN = A::FN;
   using TL = TileLds<T, TILE, TILE>;
-  int tm, tn;
-  const int ntri = p.tiles * (p.tiles + 1) / 2;
-  tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
-  const int bz = blockIdx.y;
   const int64_t ldk_bytes = (int64_t)p.ldk * sizeof(T);
   const char* Lg = reinterpret_cast<const char*>(p.L + bz * p.sL) + (int64_t)tm * TILE * ldk_bytes;
   const char* Rg = reinterpret_cast<const char*>(p.R + bz * p.sR) + (int64_t)tn * TILE * ldk_bytes;
@@ -729,20 +726,45 @@ __global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
   }
 }
 
+// Position of work-group b in a persistent grid of G work-groups (G a
+// multiple of 8): XCD x = b % 8 takes the contiguous piece
+// [x G/8, (x+1) G/8) of every G consecutive list positions.
+__device__ __forceinline__ int persistent_piece(int b, int G) { return (b % kXcds) * (G / kXcds) + b / kXcds; }
+
+// GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
+// n x n products into their own kernel symbol, so profiles list them apart.
+// One work-group per upper-triangle tile.
+template <typename T, int TILE, bool GRAM_INPUT>
+__global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
+  const int ntri = p.tiles * (p.tiles + 1) / 2;
+  int tm, tn;
+  tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
+  sym_tile<T, TILE>(p, tm, tn, blockIdx.y);
+}
+
+// Persistent form: a grid of work-groups looping over the tiles of all
+// matrices in list order, so one tile's stores drain while the next one
+// starts.  A kernel of its own: the loop's live state would push the 256
+// tile past the register file.
+template <typename T, int TILE, bool GRAM_INPUT>
+__global__ void __launch_bounds__(kThreads, 1) k_sym_loop(SymArgs<T> p) {
+  const int ntri = p.tiles * (p.tiles + 1) / 2;
+  const int total = ntri * p.batch, G = gridDim.x, piece = persistent_piece(blockIdx.x, G);
+  for (int base = 0; base + piece < total; base += G) {
+    const int pos = base + piece, bz = pos / ntri;
+    int tm, tn;
+    tri_tile(pos % ntri, p.tiles, tm, tn);
+    sym_tile<T, TILE>(p, tm, tn, bz);
+    lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
+  }
+}
+
 // Y = alpha E + gamma B (X^T)^T on TM x TN tiles: the update of both forms.
 template <typename T, typename OutT, int TM, int TN>
-__global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
+__device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn, int bz) {
   using A = Acc<T, TM, TN>;
   constexpr int FM = A::FM, FN = A::FN;
   using TL = TileLds<OutT, TM, TN>;
-  int tm, tn;
-  if (gridDim.y == 1) {
-    grouped_tile(xcd_order(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
-  } else {
-    tm = blockIdx.x / p.tiles_n;
-    tn = blockIdx.x % p.tiles_n;
-  }
-  const int bz = blockIdx.y;
   const int64_t ldb_bytes = (int64_t)p.ldb * sizeof(T);
   const int64_t ldxt_bytes = (int64_t)p.ldxt * sizeof(T);
   const char* Lg = reinterpret_cast<const char*>(p.B + bz * p.sB) + (int64_t)tm * TM * ldb_bytes;
@@ -844,6 +866,32 @@ __global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
   if (p.d_status) {
     const unsigned long long any_bad = __ballot(bad);
     if (any_bad && lane == __ffsll(any_bad) - 1) atomicOr(p.d_status, 1);
+  }
+}
+
+template <typename T, typename OutT, int TM, int TN>
+__global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
+  int tm, tn;
+  if (gridDim.y == 1) {
+    grouped_tile(xcd_order(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
+  } else {
+    tm = blockIdx.x / p.tiles_n;
+    tn = blockIdx.x % p.tiles_n;
+  }
+  nt_tile<T, OutT, TM, TN>(p, tm, tn, blockIdx.y);
+}
+
+// Persistent form of k_nt (see k_sym_loop).
+template <typename T, typename OutT, int TM, int TN>
+__global__ void __launch_bounds__(kThreads, 1) k_nt_loop(NTArgs<T, OutT> p) {
+  const int per = p.tiles_m * p.tiles_n;
+  const int total = per * p.batch, G = gridDim.x, piece = persistent_piece(blockIdx.x, G);
+  for (int base = 0; base + piece < total; base += G) {
+    const int pos = base + piece, bz = pos / per;
+    int tm, tn;
+    grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
+    nt_tile<T, OutT, TM, TN>(p, tm, tn, bz);
+    lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }
 

@@ -248,6 +248,28 @@ def test_batched_matches_oracle_and_single_calls(shape, mode):
         assert err < 1e-2, (i, err)
 
 
+@pytest.mark.parametrize("mode", ["gram", "standard"])
+def test_batched_persistent_grid_matches_single_calls(mode):
+    # 40 matrices of 512 x 1000 on 128 tiles: 400 upper-triangle tiles and
+    # 1280 update tiles per launch, so the products run as persistent grids
+    # looping over tiles of different matrices; single calls use one
+    # work-group per tile.  Results must agree bit for bit.
+    dev = _dev()
+    e = 40
+    m = workloads.gaussian((e, 512, 1000), seed=29, dtype="bf16")
+    x = m.to(dev)
+    nsa.orthogonalize_batched(x, mode=mode, tile=128)
+    torch.cuda.synchronize()
+    for i in (0, 17, e - 1):
+        single = m[i].to(dev)
+        nsa.orthogonalize(single, mode=mode, tile=128)
+        torch.cuda.synchronize()
+        assert torch.equal(single, x[i]), i
+        err = _rel(x[i].double().cpu().numpy(),
+                   _oracle(m[i].double().numpy(), mode))
+        assert err < 1e-2, (i, err)
+
+
 # ---------------------------------------------------------------------------
 # Soft-threshold split.
 # ---------------------------------------------------------------------------
