@@ -31,8 +31,8 @@ struct Plan {
   int64_t rows = 0, cols = 0, n = 0, m = 0, n_pad = 0, m_pad = 0;
   int64_t batch = 1;
   bool transposed = false;
-  int tile = 256;    // edge of the square tiles of the symmetric products (rows of nn tiles)
-  int tile_n = 256;  // columns of nn tiles
+  int tile = 256;    // edge of the square tiles of the products
+  int tile_n = 256;  // columns of the update tiles (the padding of m)
   ns_dtype io = NS_BF16, internal = NS_FP16;
   ns_mode mode = NS_STANDARD;
   int esz = 2;

@@ -15,22 +15,21 @@
 //          whose result feeds another update writes both.
 //
 // Tile engine (gfx950, CDNA4):
-//   * 256 threads = 4 wave64s in a 2 x 2 grid; block tile TM x TN (sym:
-//     square, 128, 192 or 256; nn: 128 x 128, 192 x 256 or 256 x 256); each
-//     wave owns a (TM/2) x (TN/2) sub-tile made of 32 x 32 MFMA tiles
+//   * 256 threads = 4 wave64s in a 2 x 2 grid; square block tiles of 128,
+//     192 or 256 (the same edge for both products of a call); each wave owns
+//     a (TM/2) x (TN/2) sub-tile made of 32 x 32 MFMA tiles
 //     (v_mfma_f32_32x32x16_{f16,bf16}; for fp32 operands four
 //     v_mfma_f32_32x32x2_f32 per 16-byte chunk).  The 192 edge exists for
 //     occupancy: a 4096 x 4096 symmetric product has 136 upper-triangle
 //     tiles of 256 but 253 of 192, for 256 compute units.
 //   * K is consumed in k-tiles of 128 bytes per operand row (64 16-bit or
-//     32 fp32 elements), staged through LDS with two buffers; the copies of
-//     k-tile t+2 are in flight while k-tiles t and t+1 feed the MFMAs.
+//     32 fp32 elements), copied straight from global memory into LDS stages
+//     (two or three; see Stages) and read back as MFMA fragments while the
+//     copies of later k-tiles are in flight.
 //   * LDS rows are 128 bytes made of eight 16-byte chunks; chunk c of row r
 //     lives at slot c ^ ((r ^ (r >> 3)) & 7), so the 32 rows an MFMA operand
-//     read touches, and the transposed writes of the nn loader, spread over
-//     the banks.
-//   * Both operands are read from LDS the same way (row r, 8 consecutive k)
-//     and copied straight from global memory into LDS.
+//     read touches spread over the banks.
+//   * Both operands are read from LDS the same way (row r, 8 consecutive k).
 //   * The MFMA's first operand is the right-hand matrix, so each lane ends
 //     up holding four consecutive columns of one output row, which makes the
 //     fp32 epilogue (alpha*E + gamma*acc, casts) work on 8- or 16-byte

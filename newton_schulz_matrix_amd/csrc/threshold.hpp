@@ -93,7 +93,6 @@ __global__ void __launch_bounds__(kHistThreads) k_radix_pick(SelectState* st, co
                                                             int bits, int last, float mult, float user_lambda,
                                                             float* d_lambda_out) {
   __shared__ uint64_t part[kHistThreads];
-  __shared__ int found;
   const int nb = 1 << bits;
   const int per = (nb + kHistThreads - 1) / kHistThreads;
   const int lo = threadIdx.x * per;
@@ -110,7 +109,6 @@ __global__ void __launch_bounds__(kHistThreads) k_radix_pick(SelectState* st, co
     int bin = t * per;
     const int end = min(nb, bin + per);
     while (bin < end - 1 && acc + hist[bin] < want) acc += hist[bin++];
-    found = bin;
     st->rank = want - acc;
     st->prefix |= (uint32_t)bin << shift;
     st->mask |= ((uint32_t)nb - 1u) << shift;
