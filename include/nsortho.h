@@ -127,7 +127,9 @@ size_t ns_workspace_size(int64_t rows, int64_t cols, int64_t batch,
  *
  *   X        device pointer, row-major, element (i, j) at X[i * ld + j],
  *            dtype `dtype`; read as input, overwritten with the result.
- *   rows, cols  >= 1.  The pages' n x m matrix is min x max of these.
+ *   rows, cols  >= 1.  The pages' n x m matrix is min x max of these;
+ *            n <= 65536 and m <= 2^24 (fp32 input: 2^23), else
+ *            NS_ERR_INVALID_ARG.
  *   ld       leading dimension in elements, >= cols.
  *   steps    1..NS_MAX_STEPS Newton-Schulz steps (the pages use 5).
  *   a, b, c  host arrays of `steps` floats: step k uses (a[k-1], b[k-1],

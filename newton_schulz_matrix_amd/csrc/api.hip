@@ -156,8 +156,10 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
   p->esz = elem_size(internal);
   p->x_elems = p->n_pad * p->m_pad;
   p->nn_elems = p->n_pad * p->n_pad;
-  // Offsets inside one matrix are 32-bit in the kernels' index math.
-  if ((double)p->x_elems * p->esz >= 2147483648.0 || p->n_pad > 65536) return NS_ERR_INVALID_ARG;
+  // Index math: tile counts and leading dimensions are 32-bit, and a copy
+  // instruction's per-lane offset within a k-tile panel (at most 64 rows of
+  // a row of m_pad elements) must fit in 32 bits.
+  if (p->n_pad > 65536 || p->m_pad * p->esz > (int64_t(1) << 25)) return NS_ERR_INVALID_ARG;
   // About 2048 norm blocks in total, at most one per input row.
   const int64_t want = (2048 + batch - 1) / batch;
   p->partials = (int)std::min<int64_t>(std::min<int64_t>(want, rows), kMaxPartials);

@@ -361,9 +361,14 @@ __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const 
 // acc += L-tile * R-tile^T over k-tiles [kt0, kt1) (acc is initialized by the
 // caller).  On return every copy has landed and all waves have passed a
 // barrier after their last LDS read, so the stage buffers may be reused.
-template <typename T, int TM, int TN>
+// `after_copies` runs right after the prologue's copies are issued and
+// issues `extra_loads` more vector-memory loads per thread (the epilogue
+// operand's prefetch, 0 when there is none); the first wait counts them, so
+// they do not delay the first k-tile.
+template <typename T, int TM, int TN, int kExtraLoads, class AfterCopies>
 __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, const char* Rg, int64_t ldr_bytes,
-                                         int kt0, int kt1, Acc<T, TM, TN>& acc) {
+                                         int kt0, int kt1, Acc<T, TM, TN>& acc, bool extra_loads,
+                                         AfterCopies&& after_copies) {
   constexpr int FM = TM / 64, FN = TN / 64;
   constexpr int kOffR = TM * kRowBytes;
   constexpr int kDma = TM / 32 + TN / 32;  // copy instructions per k-tile per wave
@@ -372,7 +377,10 @@ __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, cons
   static_assert((TM + TN) * kRowBytes <= S::kBytes, "stage too small");
   const int w = threadIdx.x >> 6;
   const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * (TN / 2);
-  if (kt1 <= kt0) return;
+  if (kt1 <= kt0) {
+    after_copies();
+    return;
+  }
   const int klast = kt1 - 1;
   auto clamp = [klast](int k) { return k < klast ? k : klast; };
 
@@ -393,8 +401,13 @@ __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, cons
     la.issue(Lg, clamp(kt0 + 2), S::s2());
     lb.issue(Rg, clamp(kt0 + 2), S::s2() + kOffR);
   }
-  // Copies complete in order: wait for the first k-tile only.
-  __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * kDma));
+  after_copies();
+  // Loads complete in order: wait for the first k-tile only.
+  static_assert((NS - 1) * kDma + kExtraLoads <= 63, "vmcnt has 6 bits");
+  if (extra_loads)
+    __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * kDma + kExtraLoads));
+  else
+    __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * kDma));
   lds_barrier();
   FragSets<FM, FN> fs;
   {
@@ -597,6 +610,7 @@ template <typename T, int TM, int TN>
 struct EPrefetch {
   static constexpr int FM = TM / 64, FN = TN / 64;
   static constexpr bool kEnabled = FM * FN <= 9 && sizeof(T) == 2;
+  static constexpr int kLoads = kEnabled ? FM * FN * 4 : 0;  // vector loads per thread
   uint2 v[kEnabled ? FM : 1][kEnabled ? FN : 1][4];
   __device__ __forceinline__ void load(const T* E, int64_t ld, int64_t row0, int64_t col0) {
     if constexpr (kEnabled) {
@@ -641,11 +655,12 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
   const bool diag_tile = (tm == tn);
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
-  EPrefetch<T, TILE, TILE> ep;
-  ep.load(E, p.ldn, row0, col0);
+  using EP = EPrefetch<T, TILE, TILE>;
+  EP ep;
   A acc;
   acc_zero(acc);
-  mainloop<T, TILE, TILE>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc);
+  mainloop<T, TILE, TILE, EP::kLoads>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
+                                      [&] { ep.load(E, p.ldn, row0, col0); });
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
@@ -773,11 +788,12 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   OutT* Y = p.Y + bz * p.sY;
   T* YT = p.YT ? p.YT + bz * p.sYT : nullptr;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  EPrefetch<T, TM, TN> ep;
-  ep.load(E, p.lde, row0, col0);
+  using EP = EPrefetch<T, TM, TN>;
+  EP ep;
   A acc;
   acc_zero(acc);
-  mainloop<T, TM, TN>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc);
+  mainloop<T, TM, TN, EP::kLoads>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
+                                  [&] { ep.load(E, p.lde, row0, col0); });
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;

@@ -102,6 +102,14 @@ def _padded_n(rows, cols, batch=1, mode="gram"):
     raise AssertionError(f"no forced tile reproduces the automatic plan for {n}")
 
 
+def test_largest_sizes_are_accepted():
+    # No 2 GiB cap on one matrix: a 16384 x 65536 bf16 input needs 2 GiB X
+    # buffers; n = 65536 and m = 2^24 are the limits.
+    assert nsa.workspace_size(16384, 65536, 1, torch.bfloat16, "gram") > 8 << 30
+    assert nsa.workspace_size(8, 1 << 24, 1, torch.bfloat16, "standard") > 0
+    assert nsa.workspace_size(65536, 65536, 1, torch.bfloat16, "standard") > 0
+
+
 def test_automatic_tile_choice():
     # 4096 x 4096 symmetric products: 253 tiles of 192 fill the 256 compute
     # units where 136 tiles of 256 leave half of them idle.
@@ -122,7 +130,10 @@ def test_automatic_tile_choice():
 def test_workspace_size_rejects_bad_arguments():
     lib = B.lib()
     bad = [(0, 5, 1, 0, 0), (5, 0, 1, 0, 0), (5, 5, 0, 0, 0), (5, 5, 1, 7, 0),
-           (5, 5, 1, 0, 3), (5, 5, 70000, 0, 0)]
+           (5, 5, 1, 0, 3), (5, 5, 70000, 0, 0),
+           (65537, 70000, 1, 0, 0),            # n above 65536
+           (5, (1 << 24) + 1, 1, 0, 0),        # m above 2^24 (16-bit)
+           (5, (1 << 23) + 1, 1, 2, 0)]        # m above 2^23 (fp32)
     for rows, cols, batch, dt, mode in bad:
         assert lib.ns_workspace_size(rows, cols, batch, dt, mode, None) == 0
     # fp32 input cannot use 16-bit products; bf16 input cannot use fp32.

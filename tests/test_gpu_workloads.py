@@ -127,3 +127,28 @@ def test_root_split_then_orthogonalize():
               f"{mse_gpu:.4f} (oracle {mse_ref:.4f})")
         assert err < 1e-2
         assert abs(mse_gpu - mse_ref) < 0.1 * mse_ref
+
+
+@pytest.mark.parametrize("tall", [False, True])
+def test_matrix_above_2gib_block_embedding(tall):
+    # A 16384 x 65536 bf16 matrix (2 GiB; its internal X buffers are 2 GiB
+    # too) that is zero except a ragged 200 x 300 Gaussian block A at the far
+    # corner.  M = P A Q^T with P, Q column selections, so the result is A's
+    # orthogonalization at the same place and exact zeros elsewhere: the
+    # whole path runs with offsets past 2^31 bytes, checked against the
+    # oracle on A.
+    dev = _dev()
+    rows, cols = (65536, 16384) if tall else (16384, 65536)
+    br, bc = 200, 300
+    r0, c0 = rows - br - 7, cols - bc - 5
+    a = workloads.gaussian((br, bc), seed=91, dtype="bf16")
+    x = torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev)
+    x[r0:r0 + br, c0:c0 + bc] = a.to(dev)
+    nsa.orthogonalize(x, mode="gram")
+    torch.cuda.synchronize()
+    block = x[r0:r0 + br, c0:c0 + bc].double().cpu().numpy()
+    err = _rel(block, _oracle(a.double().numpy(), "gram"))
+    print(f"{rows}x{cols} block at ({r0}, {c0}): rel err {err:.3e}")
+    assert err < 1e-2
+    x[r0:r0 + br, c0:c0 + bc] = 0
+    assert torch.count_nonzero(x).item() == 0
