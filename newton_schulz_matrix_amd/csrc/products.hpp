@@ -557,7 +557,8 @@ __device__ __forceinline__ void grouped_tile(int idx, int tiles_m, int tiles_n, 
 // kRowB bytes (kSlots 16-byte slots, the first kCPR of them used), 16-byte
 // chunk q of row r at slot q ^ tswz(r).  The swizzle keeps both the
 // row-quad writes from the accumulators (32 consecutive rows) and the
-// column reads of the transposed stores (rows 8 apart) on distinct chunks.
+// block reads of the transposed stores (the same chunk of rows 8 apart) on
+// distinct chunks.
 // The tile spans the first two stage buffers: rows [0, kRowsPerStage) in
 // the first, the rest in the second.
 template <typename T, int TM, int TN>
@@ -580,12 +581,36 @@ struct TileLds {
     return row_base(r) + (((col / kEC) ^ tswz(r)) << 4) + (col % kEC) * (int)sizeof(T);
   }
   static __device__ __forceinline__ char* chunk(int r, int c) { return row_base(r) + ((c ^ tswz(r)) << 4); }
-  // kEC consecutive rows r0.. of column col, as one 16-byte chunk.
-  static __device__ __forceinline__ uint4 column_chunk(int r0, int col) {
-    T vals[kEC];
+  // The kEC x kEC block of tile rows rb*kEC.. and columns cb*kEC.., read as
+  // kEC row chunks and transposed in registers: out[e] is column cb*kEC + e
+  // of the block, kEC consecutive tile rows in one 16-byte chunk (chunk rb
+  // of row cb*kEC + e of the transposed tile).
+  static __device__ __forceinline__ void block_t(int rb, int cb, uint4 (&out)[kEC]) {
+    uint32_t in[kEC][4];
 #pragma unroll
-    for (int e = 0; e < kEC; ++e) vals[e] = *reinterpret_cast<const T*>(at(r0 + e, col));
-    return *reinterpret_cast<const uint4*>(vals);
+    for (int i = 0; i < kEC; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(chunk(rb * kEC + i, cb));
+      in[i][0] = v.x;
+      in[i][1] = v.y;
+      in[i][2] = v.z;
+      in[i][3] = v.w;
+    }
+#pragma unroll
+    for (int c = 0; c < kEC; ++c) {
+      uint32_t d[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (sizeof(T) == 2) {
+          // Word k of the column holds rows 2k and 2k+1: the low or high
+          // halves of word c/2 of those two rows.
+          const uint32_t a = in[2 * k][c >> 1], b = in[2 * k + 1][c >> 1];
+          d[k] = (c & 1) ? (a >> 16) | (b & 0xffff0000u) : (a & 0xffffu) | (b << 16);
+        } else {
+          d[k] = in[k][c];
+        }
+      }
+      out[c] = uint4{d[0], d[1], d[2], d[3]};
+    }
   }
 };
 
@@ -697,18 +722,25 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
 
   // Phase B: rows of the tile.  On a diagonal tile each element (r, j) is
   // taken from the upper triangle, tile[min(r, j)][max(r, j)], so the result
-  // is exactly symmetric; C2's diagonal was written in phase A.
+  // is exactly symmetric; C2's diagonal was written in phase A.  Every
+  // thread handles the same number of chunks, so the off-diagonal loop is
+  // unrolled and its LDS reads overlap.
   constexpr int kChunks = TILE * TL::kCPR;
   constexpr int EC = TL::kEC;
-  for (int q = threadIdx.x; q < kChunks; q += kThreads) {
-    const int r = q / TL::kCPR, c = q % TL::kCPR;
-    T* dst = C + (row0 + r) * p.ldn + col0 + c * EC;
-    T* dst2 = C2 ? C2 + (row0 + r) * p.ldn + col0 + c * EC : nullptr;
-    if (!diag_tile) {
+  static_assert(kChunks % kThreads == 0, "whole chunks per thread");
+  if (!diag_tile) {
+#pragma unroll 6
+    for (int it = 0; it < kChunks / kThreads; ++it) {
+      const int q = it * kThreads + threadIdx.x;
+      const int r = q / TL::kCPR, c = q % TL::kCPR;
       const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
-      *reinterpret_cast<uint4*>(dst) = val;
-      if (dst2) *reinterpret_cast<uint4*>(dst2) = val;
-    } else {
+      *reinterpret_cast<uint4*>(C + (row0 + r) * p.ldn + col0 + c * EC) = val;
+      if (C2) *reinterpret_cast<uint4*>(C2 + (row0 + r) * p.ldn + col0 + c * EC) = val;
+    }
+  } else {
+    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
+      const int r = q / TL::kCPR, c = q % TL::kCPR;
+      T* dst = C + (row0 + r) * p.ldn + col0 + c * EC;
       T vals[EC];
 #pragma unroll
       for (int e = 0; e < EC; ++e) {
@@ -716,7 +748,8 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
         vals[e] = *reinterpret_cast<const T*>(j >= r ? TL::at(r, j) : TL::at(j, r));
       }
       *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
-      if (dst2) {
+      if (C2) {
+        T* dst2 = C2 + (row0 + r) * p.ldn + col0 + c * EC;
         const int jd = r - c * EC;  // position of the diagonal inside this chunk
         if (jd >= 0 && jd < EC && row0 + r < p.n_real) {
 #pragma unroll
@@ -727,16 +760,29 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
         }
       }
     }
+    return;
   }
-  if (diag_tile) return;
 
-  // Phase C: the mirrored tile, C[col0 + jj][row0 + i] = tile[i][jj]; row jj
-  // of the mirror is column jj of the LDS tile.
-  for (int q = threadIdx.x; q < kChunks; q += kThreads) {
-    const int jj = q / TL::kCPR, c = q % TL::kCPR;
-    const uint4 val = TL::column_chunk(c * EC, jj);
-    *reinterpret_cast<uint4*>(C + (col0 + jj) * p.ldn + row0 + c * EC) = val;
-    if (C2) *reinterpret_cast<uint4*>(C2 + (col0 + jj) * p.ldn + row0 + c * EC) = val;
+  // Phase C: the mirrored tile, C[col0 + j][row0 + i] = tile[i][j], from
+  // EC x EC blocks transposed in registers.  Block (rb, cb) gives chunk rb of
+  // mirrored rows cb*EC .. cb*EC + EC - 1; consecutive threads take
+  // consecutive rb, so each mirrored row is written as adjacent chunks.
+  constexpr int kB = TL::kCPR;  // blocks along a tile edge
+  constexpr int kBlocks = kB * kB;
+#pragma unroll 1
+  for (int it = 0; it < (kBlocks + kThreads - 1) / kThreads; ++it) {
+    const int q = it * kThreads + threadIdx.x;
+    if (kBlocks % kThreads == 0 || q < kBlocks) {
+      const int rb = q % kB, cb = q / kB;
+      uint4 cols[EC];
+      TL::block_t(rb, cb, cols);
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        const int64_t off = (col0 + cb * EC + e) * p.ldn + row0 + rb * EC;
+        *reinterpret_cast<uint4*>(C + off) = cols[e];
+        if (C2) *reinterpret_cast<uint4*>(C2 + off) = cols[e];
+      }
+    }
   }
 }
 
@@ -829,25 +875,43 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   __syncthreads();
 
   constexpr int kEC = TL::kEC;
-  constexpr int kColChunks = TM / kEC;  // chunks of a tile column
+  constexpr int kChunks = TM * TL::kCPR;  // row chunks of the tile
+  static_assert(kChunks % kThreads == 0, "whole chunks per thread");
+  // EC x EC blocks for the transposed stores (see TileLds::block_t): block
+  // q covers tile rows rb*kEC.. and columns cb*kEC.., consecutive threads
+  // take consecutive rb, so a transposed row is written as adjacent chunks.
+  constexpr int kRB = TM / kEC, kBlocks = kRB * TL::kCPR;
+  constexpr int kBIters = (kBlocks + kThreads - 1) / kThreads;
   if (!p.final_out) {
     // Internal buffers: the whole padded tile, rows of Y and, when asked,
     // rows of Y^T (columns of the tile).
-    for (int q = threadIdx.x; q < TM * TL::kCPR; q += kThreads) {
+#pragma unroll 6
+    for (int it = 0; it < kChunks / kThreads; ++it) {
+      const int q = it * kThreads + threadIdx.x;
       const int r = q / TL::kCPR, c = q % TL::kCPR;
       *reinterpret_cast<uint4*>(Y + (row0 + r) * p.ldy + col0 + c * kEC) =
           *reinterpret_cast<const uint4*>(TL::chunk(r, c));
     }
     if (YT) {
-      for (int q = threadIdx.x; q < TN * kColChunks; q += kThreads) {
-        const int jj = q / kColChunks, c = q % kColChunks;
-        *reinterpret_cast<uint4*>(YT + (col0 + jj) * p.ldyt + row0 + c * kEC) = TL::column_chunk(c * kEC, jj);
+#pragma unroll 1
+      for (int it = 0; it < kBIters; ++it) {
+        const int q = it * kThreads + threadIdx.x;
+        if (kBlocks % kThreads == 0 || q < kBlocks) {
+          const int rb = q % kRB, cb = q / kRB;
+          uint4 cols[kEC];
+          TL::block_t(rb, cb, cols);
+#pragma unroll
+          for (int e = 0; e < kEC; ++e)
+            *reinterpret_cast<uint4*>(YT + (col0 + cb * kEC + e) * p.ldyt + row0 + rb * kEC) = cols[e];
+        }
       }
     }
   } else if (!p.transpose_out) {
     // Caller's matrix, same orientation: rows i < n_real, columns j < m_real.
     const bool vec = (p.ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
-    for (int q = threadIdx.x; q < TM * TL::kCPR; q += kThreads) {
+#pragma unroll 6
+    for (int it = 0; it < kChunks / kThreads; ++it) {
+      const int q = it * kThreads + threadIdx.x;
       const int r = q / TL::kCPR, c = q % TL::kCPR;
       const int64_t i = row0 + r, j0 = col0 + c * kEC;
       if (i >= p.n_real || j0 >= p.m_real) continue;
@@ -864,17 +928,26 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
     // Caller's matrix is the transpose: its row j holds tile column j, in
     // TM / kEC chunks of kEC tile rows.
     const bool vec = (p.ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
-    for (int q = threadIdx.x; q < TN * kColChunks; q += kThreads) {
-      const int jj = q / kColChunks, c = q % kColChunks;
-      const int64_t j = col0 + jj, i0 = row0 + c * kEC;
-      if (j >= p.m_real || i0 >= p.n_real) continue;
-      const uint4 val = TL::column_chunk(c * kEC, jj);
-      OutT* dst = Y + j * p.ldy + i0;
-      if (vec && i0 + kEC <= p.n_real) {
-        final_chunk(dst, val, p.accumulate, p.apply_scale);
-      } else {
-        const OutT* vals = reinterpret_cast<const OutT*>(&val);
-        for (int e = 0; e < kEC && i0 + e < p.n_real; ++e) final_elem(dst + e, vals[e], p.accumulate, p.apply_scale);
+#pragma unroll 1
+    for (int it = 0; it < kBIters; ++it) {
+      const int q = it * kThreads + threadIdx.x;
+      if (kBlocks % kThreads != 0 && q >= kBlocks) continue;
+      const int rb = q % kRB, cb = q / kRB;
+      const int64_t i0 = row0 + rb * kEC;
+      if (i0 >= p.n_real) continue;
+      uint4 cols[kEC];
+      TL::block_t(rb, cb, cols);
+#pragma unroll
+      for (int e = 0; e < kEC; ++e) {
+        const int64_t j = col0 + cb * kEC + e;
+        if (j >= p.m_real) continue;
+        OutT* dst = Y + j * p.ldy + i0;
+        if (vec && i0 + kEC <= p.n_real) {
+          final_chunk(dst, cols[e], p.accumulate, p.apply_scale);
+        } else {
+          const OutT* vals = reinterpret_cast<const OutT*>(&cols[e]);
+          for (int k = 0; k < kEC && i0 + k < p.n_real; ++k) final_elem(dst + k, vals[k], p.accumulate, p.apply_scale);
+        }
       }
     }
   }
