@@ -97,7 +97,16 @@ bool use_persistent(int edge, int64_t tiles, int64_t ktiles) {
   return edge <= 192 && tiles > kPersistentGroups && ktiles <= kPersistentMaxKtiles;
 }
 
-double product_estimate(int edge, double tiles, double ktiles, double per_ktile, double fixed) {
+// Launches that take the two-work-groups-per-CU kernels (16-bit, 128 tiles,
+// at least 512 tiles; see use_pair): per pair of tiles on a CU, measured on
+// MI355X against the table above on the 128 x 1408 x 2048 expert batch.
+constexpr double kPairKtile = 0.79, kPairSymFixed = 4.9, kPairNnFixed = 5.7;
+
+bool use_pair(int edge, int esz, int64_t tiles);
+
+double product_estimate(int edge, double tiles, double ktiles, double per_ktile, double fixed,
+                        double pair_fixed) {
+  if (use_pair(edge, 2, (int64_t)tiles)) return ceil(tiles / (2 * kComputeUnits)) * (ktiles * kPairKtile + pair_fixed);
   const double waves = ceil(tiles / kComputeUnits);
   if (use_persistent(edge, (int64_t)tiles, (int64_t)ktiles)) fixed *= kPersistentFixed;
   return waves * (ktiles * per_ktile + fixed);
@@ -108,9 +117,9 @@ double tile_estimate(const TileCost& c, int64_t n, int64_t m, int64_t batch, ns_
   const double nt = (double)(n_pad / c.edge), b = (double)batch;
   const double sym_tiles = nt * (nt + 1) / 2 * b, nn_tiles = nt * (double)(m_pad / tn) * b;
   const double kn = ceil((double)n / 64), km = ceil((double)m / 64);  // contractions stop at the real size
-  const double sym = product_estimate(c.edge, sym_tiles, kn, c.sym_ktile, c.sym_fixed);
-  const double gram = product_estimate(c.edge, sym_tiles, km, c.sym_ktile, c.sym_fixed);
-  const double nn = product_estimate(c.edge, nn_tiles, kn, c.nn_ktile, c.nn_fixed);
+  const double sym = product_estimate(c.edge, sym_tiles, kn, c.sym_ktile, c.sym_fixed, kPairSymFixed);
+  const double gram = product_estimate(c.edge, sym_tiles, km, c.sym_ktile, c.sym_fixed, kPairSymFixed);
+  const double nn = product_estimate(c.edge, nn_tiles, kn, c.nn_ktile, c.nn_fixed, kPairNnFixed);
   // Launch counts of five steps: standard 5 X X^T, 5 n x n, 5 updates; Gram
   // (one restart) 2 X X^T, about 14 n x n products and 2 updates.
   return mode == NS_GRAM ? 2 * gram + 14 * sym + 2 * nn : 5 * (gram + sym + nn);
@@ -216,14 +225,36 @@ struct Tracer {
 // runs as a persistent grid of kPersistentGroups work-groups (one per CU of
 // MI355X) that loop over the tiles, so one tile's stores drain while the
 // next one starts; other launches get one work-group per tile.  The 256 tile
-// has no persistent kernel (its registers are full).  Correctness does not
-// depend on the CU count.
+// has no persistent kernel (its registers are full).  16-bit products on 128
+// tiles with at least two work-groups' worth of tiles per CU use the kernels
+// built for two work-groups per CU (two LDS stages), where one work-group's
+// start-up and epilogue overlap the other's main loop; the update's loop
+// kernel does not fit that register budget, so it runs one work-group per
+// tile.  Correctness does not depend on the CU count.
+template <typename T, int TILE>
+constexpr bool kHasPairKernels = TILE == 128 && sizeof(T) == 2;
+
+bool use_pair(int edge, int esz, int64_t tiles) {
+  return edge == 128 && esz == 2 && tiles >= 2 * (int64_t)kPersistentGroups;
+}
+
 template <typename T, int TILE, bool GRAM_INPUT>
 hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s) {
   const int64_t ntri = (int64_t)a.tiles * (a.tiles + 1) / 2;
+  const int ktiles = a.K / (kRowBytes / (int)sizeof(T));
   a.batch = (int)batch;
+  if constexpr (kHasPairKernels<T, TILE>) {
+    if (use_pair(TILE, (int)sizeof(T), ntri * batch)) {
+      if (use_persistent(TILE, ntri * batch, ktiles))
+        hipLaunchKernelGGL((k_sym_loop<T, TILE, GRAM_INPUT, 2>), dim3(2 * kPersistentGroups), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT, 2>), dim3((unsigned)ntri, (unsigned)batch), dim3(kThreads), 0,
+                           s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (TILE <= 192) {
-    if (use_persistent(TILE, ntri * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
+    if (use_persistent(TILE, ntri * batch, ktiles)) {
       hipLaunchKernelGGL((k_sym_loop<T, TILE, GRAM_INPUT>), dim3(kPersistentGroups), dim3(kThreads), 0, s, a);
       return hipGetLastError();
     }
@@ -236,6 +267,13 @@ template <typename T, typename OutT, int TILE>
 hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s) {
   const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
   a.batch = (int)batch;
+  if constexpr (kHasPairKernels<T, TILE>) {
+    if (use_pair(TILE, (int)sizeof(T), per * batch)) {
+      hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE), 2>), dim3((unsigned)per, (unsigned)batch),
+                         dim3(kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (TILE <= 192) {
     if (use_persistent(TILE, per * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
       hipLaunchKernelGGL((k_nt_loop<T, OutT, TILE, nn_tile_n(TILE)>), dim3(kPersistentGroups), dim3(kThreads), 0,

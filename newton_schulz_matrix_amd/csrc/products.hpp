@@ -228,8 +228,9 @@ struct Acc {
 // wait for the copies in flight before every read.  A stage holds the L
 // operand (TM rows x 128 bytes) followed by the R operand (TN rows).  Three
 // families: 64 KiB stages (two; tiles of 256 + 256 or 192 + 256 rows), 48 KiB
-// (three; 192 + 192) and 32 KiB (three; 128 + 128).  Three stages, where
-// they fit in LDS, give every copy two pipeline steps to land.
+// (three; 192 + 192) and 32 KiB (three, or two in the kernels built for two
+// work-groups per compute unit; 128 + 128).  Three stages, where they fit in
+// LDS, give every copy two pipeline steps to land.
 __shared__ __attribute__((aligned(1024))) char g_stage0_big[65536];
 __shared__ __attribute__((aligned(1024))) char g_stage1_big[65536];
 __shared__ __attribute__((aligned(1024))) char g_stage0_mid[49152];
@@ -258,11 +259,15 @@ template <> struct StageMem<32768> {
 
 constexpr int kLdsBytes = 160 * 1024;
 
-template <int TM, int TN>
+// G is the number of work-groups a kernel is built to share a compute unit
+// with: G = 2 takes two stages (two 128-tile work-groups then fit in LDS
+// together, and one's start-up and epilogue overlap the other's main loop).
+template <int TM, int TN, int G = 1>
 struct Stages {
   static constexpr int kNeed = (TM + TN) * kRowBytes;
   static constexpr int kBytes = kNeed > 49152 ? 65536 : kNeed > 32768 ? 49152 : 32768;
-  static constexpr int kCount = 3 * kBytes <= kLdsBytes ? 3 : 2;
+  static constexpr int kCount = G == 1 && 3 * kBytes <= kLdsBytes ? 3 : 2;
+  static_assert(G == 1 || G * kCount * kBytes <= kLdsBytes, "G work-groups must fit in LDS");
   using M = StageMem<kBytes>;
   static __device__ __forceinline__ char* s0() { return M::s0(); }
   static __device__ __forceinline__ char* s1() { return M::s1(); }
@@ -307,13 +312,13 @@ __device__ __forceinline__ void schedule_half() {
   }
 }
 
-template <typename T, int TM, int TN>
+template <typename T, int TM, int TN, int G>
 __device__ __forceinline__ void schedule_step() {
   constexpr int FM = TM / 64, FN = TN / 64;
   constexpr int NR = 2 * (FM + FN);                               // reads per half
   constexpr int NM = 2 * FM * FN * (sizeof(T) == 4 ? 4 : 1);      // MFMAs per half
   constexpr int NV = TM / 32 + TN / 32;                           // copies per step
-  constexpr int NV1 = Stages<TM, TN>::kCount == 3 ? (NV + 1) / 2 : NV;
+  constexpr int NV1 = Stages<TM, TN, G>::kCount == 3 ? (NV + 1) / 2 : NV;
   static_assert(NM >= NR, "at least one MFMA per read");
   schedule_half<NM, NR, NV1, 0>();
   schedule_half<NM, NR, NV - NV1, 0>();
@@ -330,7 +335,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int TM, int TN>
+template <typename T, int TM, int TN, int G>
 __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const DmaLoader<TM>& la,
                                           const DmaLoader<TN>& lb, int kt_copy, char* __restrict__ D,
                                           const char* __restrict__ P, const FragAddr& fa,
@@ -347,11 +352,11 @@ __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const 
   load_frags<FM, FN>(P, P + kOffR, fa, 3, fs.f3);
   mma_frags<T, FM, FN>(fs.f0, acc);
   mma_frags<T, FM, FN>(fs.f1, acc);
-  schedule_step<T, TM, TN>();
+  schedule_step<T, TM, TN, G>();
   // With three stages the copy just issued may stay in flight (it lands in
   // a stage read two steps later); the one issued a step ago must be
   // complete.
-  if constexpr (Stages<TM, TN>::kCount == 3)
+  if constexpr (Stages<TM, TN, G>::kCount == 3)
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(TM / 32 + TN / 32));
   else
     __builtin_amdgcn_s_waitcnt(0);
@@ -365,14 +370,14 @@ __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const 
 // issues `extra_loads` more vector-memory loads per thread (the epilogue
 // operand's prefetch, 0 when there is none); the first wait counts them, so
 // they do not delay the first k-tile.
-template <typename T, int TM, int TN, int kExtraLoads, class AfterCopies>
+template <typename T, int TM, int TN, int kExtraLoads, int G, class AfterCopies>
 __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, const char* Rg, int64_t ldr_bytes,
                                          int kt0, int kt1, Acc<T, TM, TN>& acc, bool extra_loads,
                                          AfterCopies&& after_copies) {
   constexpr int FM = TM / 64, FN = TN / 64;
   constexpr int kOffR = TM * kRowBytes;
   constexpr int kDma = TM / 32 + TN / 32;  // copy instructions per k-tile per wave
-  using S = Stages<TM, TN>;
+  using S = Stages<TM, TN, G>;
   constexpr int NS = S::kCount;
   static_assert((TM + TN) * kRowBytes <= S::kBytes, "stage too small");
   const int w = threadIdx.x >> 6;
@@ -427,7 +432,7 @@ __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, cons
   // three so that every step names its stages directly (the compiler then
   // sees that a step's reads and its copies touch different objects).
   auto step = [&](int t, char* D, const char* P) {
-    pipe_step<T, TM, TN>(Lg, Rg, la, lb, clamp(t + NS), D, P, fa, fs, acc.v);
+    pipe_step<T, TM, TN, G>(Lg, Rg, la, lb, clamp(t + NS), D, P, fa, fs, acc.v);
   };
   if constexpr (NS == 3) {
     int t = kt0;
@@ -561,9 +566,9 @@ __device__ __forceinline__ void grouped_tile(int idx, int tiles_m, int tiles_n, 
 // distinct chunks.
 // The tile spans the first two stage buffers: rows [0, kRowsPerStage) in
 // the first, the rest in the second.
-template <typename T, int TM, int TN>
+template <typename T, int TM, int TN, int G>
 struct TileLds {
-  using S = Stages<TM, TN>;
+  using S = Stages<TM, TN, G>;
   static constexpr int kRowData = TN * (int)sizeof(T);
   static constexpr int kRowB = kRowData <= 256 ? 256 : 512;
   static constexpr int kSlots = kRowB / 16;
@@ -666,11 +671,11 @@ struct EPrefetch {
 };
 
 // One upper-triangle tile (tm <= tn) of matrix bz of a symmetric product.
-template <typename T, int TILE>
+template <typename T, int TILE, int G>
 __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, int bz) {
   using A = Acc<T, TILE, TILE>;
   constexpr int FM = A::FM, FN = A::FN;
-  using TL = TileLds<T, TILE, TILE>;
+  using TL = TileLds<T, TILE, TILE, G>;
   const int64_t ldk_bytes = (int64_t)p.ldk * sizeof(T);
   const char* Lg = reinterpret_cast<const char*>(p.L + bz * p.sL) + (int64_t)tm * TILE * ldk_bytes;
   const char* Rg = reinterpret_cast<const char*>(p.R + bz * p.sR) + (int64_t)tn * TILE * ldk_bytes;
@@ -684,7 +689,7 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
   EP ep;
   A acc;
   acc_zero(acc);
-  mainloop<T, TILE, TILE, EP::kLoads>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
+  mainloop<T, TILE, TILE, EP::kLoads, G>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
                                       [&] { ep.load(E, p.ldn, row0, col0); });
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -794,37 +799,37 @@ __device__ __forceinline__ int persistent_piece(int b, int G) { return (b % kXcd
 // GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
 // n x n products into their own kernel symbol, so profiles list them apart.
 // One work-group per upper-triangle tile.
-template <typename T, int TILE, bool GRAM_INPUT>
-__global__ void __launch_bounds__(kThreads, 1) k_sym(SymArgs<T> p) {
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1>
+__global__ void __launch_bounds__(kThreads, G) k_sym(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   int tm, tn;
   tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
-  sym_tile<T, TILE>(p, tm, tn, blockIdx.y);
+  sym_tile<T, TILE, G>(p, tm, tn, blockIdx.y);
 }
 
 // Persistent form: a grid of work-groups looping over the tiles of all
 // matrices in list order, so one tile's stores drain while the next one
 // starts.  A kernel of its own: the loop's live state would push the 256
 // tile past the register file.
-template <typename T, int TILE, bool GRAM_INPUT>
-__global__ void __launch_bounds__(kThreads, 1) k_sym_loop(SymArgs<T> p) {
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1>
+__global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
-  const int total = ntri * p.batch, G = gridDim.x, piece = persistent_piece(blockIdx.x, G);
-  for (int base = 0; base + piece < total; base += G) {
+  const int total = ntri * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
+  for (int base = 0; base + piece < total; base += groups) {
     const int pos = base + piece, bz = pos / ntri;
     int tm, tn;
     tri_tile(pos % ntri, p.tiles, tm, tn);
-    sym_tile<T, TILE>(p, tm, tn, bz);
+    sym_tile<T, TILE, G>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }
 
 // Y = alpha E + gamma B (X^T)^T on TM x TN tiles: the update of both forms.
-template <typename T, typename OutT, int TM, int TN>
+template <typename T, typename OutT, int TM, int TN, int G>
 __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn, int bz) {
   using A = Acc<T, TM, TN>;
   constexpr int FM = A::FM, FN = A::FN;
-  using TL = TileLds<OutT, TM, TN>;
+  using TL = TileLds<OutT, TM, TN, G>;
   const int64_t ldb_bytes = (int64_t)p.ldb * sizeof(T);
   const int64_t ldxt_bytes = (int64_t)p.ldxt * sizeof(T);
   const char* Lg = reinterpret_cast<const char*>(p.B + bz * p.sB) + (int64_t)tm * TM * ldb_bytes;
@@ -838,7 +843,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   EP ep;
   A acc;
   acc_zero(acc);
-  mainloop<T, TM, TN, EP::kLoads>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
+  mainloop<T, TM, TN, EP::kLoads, G>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
                                   [&] { ep.load(E, p.lde, row0, col0); });
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -957,8 +962,8 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   }
 }
 
-template <typename T, typename OutT, int TM, int TN>
-__global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
+template <typename T, typename OutT, int TM, int TN, int G = 1>
+__global__ void __launch_bounds__(kThreads, G) k_nt(NTArgs<T, OutT> p) {
   int tm, tn;
   if (gridDim.y == 1) {
     grouped_tile(xcd_order(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
@@ -966,19 +971,19 @@ __global__ void __launch_bounds__(kThreads, 1) k_nt(NTArgs<T, OutT> p) {
     tm = blockIdx.x / p.tiles_n;
     tn = blockIdx.x % p.tiles_n;
   }
-  nt_tile<T, OutT, TM, TN>(p, tm, tn, blockIdx.y);
+  nt_tile<T, OutT, TM, TN, G>(p, tm, tn, blockIdx.y);
 }
 
 // Persistent form of k_nt (see k_sym_loop).
-template <typename T, typename OutT, int TM, int TN>
-__global__ void __launch_bounds__(kThreads, 1) k_nt_loop(NTArgs<T, OutT> p) {
+template <typename T, typename OutT, int TM, int TN, int G = 1>
+__global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
-  const int total = per * p.batch, G = gridDim.x, piece = persistent_piece(blockIdx.x, G);
-  for (int base = 0; base + piece < total; base += G) {
+  const int total = per * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
+  for (int base = 0; base + piece < total; base += groups) {
     const int pos = base + piece, bz = pos / per;
     int tm, tn;
     grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-    nt_tile<T, OutT, TM, TN>(p, tm, tn, bz);
+    nt_tile<T, OutT, TM, TN, G>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }
