@@ -157,7 +157,9 @@ ns_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld,
  * showapi.com, section on many experts in one kernel, and the Kimi K2 expert
  * shapes in the Gram-NS article's "Performance comparison" section).
  * Matrix e starts at X + e * batch_stride elements; other arguments as for
- * ns_orthogonalize.  batch_stride >= rows * ld.
+ * ns_orthogonalize.  batch_stride >= rows * ld; 1 <= batch <= 65535, and
+ * batch * ceil(n / 128) * ceil(m / 128) < 2^31 (the update's tile count),
+ * else NS_ERR_INVALID_ARG.
  */
 ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows,
                                    int64_t cols, int64_t ld,

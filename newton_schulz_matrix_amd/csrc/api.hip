@@ -169,6 +169,9 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
   // instruction's per-lane offset within a k-tile panel (at most 64 rows of
   // a row of m_pad elements) must fit in 32 bits.
   if (p->n_pad > 65536 || p->m_pad * p->esz > (int64_t(1) << 25)) return NS_ERR_INVALID_ARG;
+  // The update's grid is one-dimensional over the tiles of all matrices (the
+  // bound is taken at the smallest tile edge, so it holds for every plan).
+  if (batch * ((p->n + 127) / 128) * ((p->m + 127) / 128) > INT32_MAX) return NS_ERR_INVALID_ARG;
   // About 2048 norm blocks in total, at most one per input row.
   const int64_t want = (2048 + batch - 1) / batch;
   p->partials = (int)std::min<int64_t>(std::min<int64_t>(want, rows), kMaxPartials);
@@ -269,8 +272,8 @@ hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s) {
   a.batch = (int)batch;
   if constexpr (kHasPairKernels<T, TILE>) {
     if (use_pair(TILE, (int)sizeof(T), per * batch)) {
-      hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE), 2>), dim3((unsigned)per, (unsigned)batch),
-                         dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE), 2>), dim3((unsigned)(per * batch)), dim3(kThreads), 0,
+                         s, a);
       return hipGetLastError();
     }
   }
@@ -281,8 +284,7 @@ hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE)>), dim3((unsigned)per, (unsigned)batch), dim3(kThreads),
-                     0, s, a);
+  hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE)>), dim3((unsigned)(per * batch)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -962,16 +962,16 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   }
 }
 
+// One work-group per tile on a one-dimensional grid over the tiles of all
+// matrices: the list (matrix by matrix, each in grouped_tile order) is cut
+// into one contiguous piece per XCD.
 template <typename T, typename OutT, int TM, int TN, int G = 1>
 __global__ void __launch_bounds__(kThreads, G) k_nt(NTArgs<T, OutT> p) {
+  const int per = p.tiles_m * p.tiles_n;
+  const int pos = xcd_order(blockIdx.x, per * p.batch);
   int tm, tn;
-  if (gridDim.y == 1) {
-    grouped_tile(xcd_order(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, tm, tn);
-  } else {
-    tm = blockIdx.x / p.tiles_n;
-    tn = blockIdx.x % p.tiles_n;
-  }
-  nt_tile<T, OutT, TM, TN, G>(p, tm, tn, blockIdx.y);
+  grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
+  nt_tile<T, OutT, TM, TN, G>(p, tm, tn, pos / per);
 }
 
 // Persistent form of k_nt (see k_sym_loop).

@@ -114,8 +114,11 @@ def test_automatic_tile_choice():
     # 4096 x 4096 symmetric products: 253 tiles of 192 fill the 256 compute
     # units where 136 tiles of 256 leave half of them idle.
     assert _padded_n(4096, 14336) == 192
-    # Small matrices use 128.
+    # Small matrices use 128, and so does the 128-expert MoE batch (1408 is
+    # a multiple of 128, and its launches take the two-work-groups-per-CU
+    # kernels).
     assert _padded_n(300, 500) == 128
+    assert _padded_n(2048, 1408, 128) == 128
     # Forced tiles: fp32 products take 128 only; unknown edges are refused.
     lib = B.lib()
     for tile in (64, 200, 512):
@@ -184,6 +187,9 @@ def test_batched_argument_checks():
                                       B.NS_BF16, 5, a, b, c, B.NS_GRAM, None,
                                       ctypes.c_void_p(256), 1 << 40, None)
     assert st == 1
+    # The update's one-dimensional grid: batch * (n/128) * (m/128) < 2^31.
+    assert lib.ns_workspace_size(8192, 1 << 20, 65535, B.NS_BF16, 1, None) == 0
+    assert lib.ns_workspace_size(8192, 1 << 20, 255, B.NS_BF16, 1, None) > 0
 
 
 def test_soft_threshold_argument_checks():

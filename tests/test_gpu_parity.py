@@ -249,13 +249,17 @@ def test_batched_matches_oracle_and_single_calls(shape, mode):
 
 
 @pytest.mark.parametrize("mode", ["gram", "standard"])
-def test_batched_persistent_grid_matches_single_calls(mode):
-    # 40 matrices of 512 x 1000 on 128 tiles: 400 upper-triangle tiles and
-    # 1280 update tiles per launch, so the products run as persistent grids
-    # looping over tiles of different matrices; single calls use one
-    # work-group per tile.  Results must agree bit for bit.
+@pytest.mark.parametrize("e", [40, 60])
+def test_batched_persistent_grid_matches_single_calls(mode, e):
+    # e matrices of 512 x 1000 on 128 tiles: 10 upper-triangle tiles and 32
+    # update tiles per matrix.  With 40, the symmetric products (400 tiles)
+    # run as a persistent grid looping over tiles of different matrices on
+    # the one-work-group-per-CU kernels and the updates (1280 tiles) on the
+    # two-work-groups-per-CU kernels; with 60, the symmetric products (600
+    # tiles) take the two-per-CU persistent grid too.  Single calls use one
+    # work-group per tile and the one-per-CU kernels.  Results must agree
+    # bit for bit.
     dev = _dev()
-    e = 40
     m = workloads.gaussian((e, 512, 1000), seed=29, dtype="bf16")
     x = m.to(dev)
     nsa.orthogonalize_batched(x, mode=mode, tile=128)
