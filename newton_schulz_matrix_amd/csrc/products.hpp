@@ -125,37 +125,58 @@ template <> __device__ __forceinline__ void mma_chunk<float>(const uint4& a, con
 // ---------------------------------------------------------------------------
 
 // K-contiguous operand: ROWS rows of 128 bytes per k-tile, copied straight
-// from global memory into LDS (global_load_lds_dwordx4: lane L of a wave
+// from global memory into LDS (buffer_load_dwordx4 ... lds: lane L of a wave
 // writes its 16 bytes at M0 + 16 L).  One instruction fills 8 LDS rows; lane
 // L fetches the chunk that belongs at slot L & 7 of row L >> 3, so the LDS
 // swizzle is applied on the global side.  Row r = 8 q + (L >> 3) of the wave
 // has swz(r) = (L >> 3) ^ (q & 7).
+//
+// Each wave addresses its rows through a buffer resource whose base is its
+// first row, a per-lane 32-bit offset per row group (fixed for the whole
+// loop) and the k-tile's byte offset as the scalar offset, so a copy costs
+// no vector address arithmetic.  The offsets stay below 2^32: a wave covers
+// at most 64 rows of at most 2^25 bytes (the plan's limit on a row).
 template <int ROWS>
 struct DmaLoader {
   static_assert(ROWS % 32 == 0, "each wave fills whole groups of 8 rows");
   static constexpr int kRowsPerWave = ROWS / 4;
   static constexpr int kIters = kRowsPerWave / 8;
-  uint32_t lane_off;   // (L >> 3) * ld + 16 * ((L & 7) ^ (L >> 3))
-  uint32_t ld8;        // 8 * ld (bytes), uniform
-  int wave_row0;       // first LDS row this wave fills (uniform)
-  __device__ __forceinline__ void init(int64_t ld_bytes) {
+  static_assert(kRowsPerWave <= 64, "per-lane offsets fit 32 bits for rows of up to 2^25 bytes");
+  // The 256 tile has no registers to spare for eight offsets; it forms each
+  // one at issue time (two 32-bit operations).
+  static constexpr bool kKeep = kIters <= 6;
+  __amdgpu_buffer_rsrc_t rsrc;       // this wave's rows of the operand tile (uniform)
+  uint32_t voff[kKeep ? kIters : 1]; // lane offset of row group i, chunk swizzle applied
+  uint32_t lane_off, ld8;            // for kKeep == false
+  int wave_row0;                     // first LDS row this wave fills (uniform)
+  __device__ __forceinline__ uint32_t offset(int i) const {
+    const int q = (wave_row0 >> 3) + i;  // LDS row group
+    // The chunk XOR for this row group: (q & 7) on bits 4-6 (the row part of
+    // the offset is a multiple of 256 bytes).
+    return (lane_off + (uint32_t)i * ld8) ^ (uint32_t)((q & 7) << 4);
+  }
+  // g: operand tile base (its first row), ld_bytes: row stride.
+  __device__ __forceinline__ void init(const char* g, int64_t ld_bytes) {
     const int lane = threadIdx.x & 63;
     wave_row0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kRowsPerWave;
+    // Word 3 of the resource: the raw (untyped) buffer format; no bounds
+    // limit below 2^32 bytes.
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(g) + (int64_t)wave_row0 * ld_bytes, (short)0, -1,
+                                             0x00020000);
     lane_off = (uint32_t)((lane >> 3) * ld_bytes) + (uint32_t)((((lane & 7) ^ (lane >> 3))) << 4);
     ld8 = (uint32_t)(8 * ld_bytes);
+    if constexpr (kKeep) {
+#pragma unroll
+      for (int i = 0; i < kIters; ++i) voff[i] = offset(i);
+    }
   }
-  // g: operand tile base (rows of this tile), kt: k-tile, lds_op: LDS base
-  // of the operand in the stage being filled.
-  __device__ __forceinline__ void issue(const char* g, int kt, char* lds_op) const {
-    const char* gw = g + (int64_t)wave_row0 * (ld8 >> 3) + (int64_t)kt * kRowBytes;
+  // kt: k-tile, lds_op: LDS base of the operand in the stage being filled.
+  __device__ __forceinline__ void issue(int kt, char* lds_op) const {
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
       const int q = (wave_row0 >> 3) + i;  // LDS row group, uniform
-      const uint32_t off = lane_off + (uint32_t)i * ld8;
-      // The chunk XOR for this row group: (q & 7) applied to the low bits.
-      const uint32_t sw = (uint32_t)((q & 7) << 4);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(gw + (off ^ sw)),
-                                       (lds_void_t*)(lds_op + q * 8 * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_op + q * 8 * kRowBytes), 16,
+                                               (int)(kKeep ? voff[i] : offset(i)), kt * kRowBytes, 0, 0);
     }
   }
 };
@@ -342,8 +363,8 @@ __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const 
                                           FragSets<TM / 64, TN / 64>& fs, f32x16 (&acc)[TM / 64][TN / 64]) {
   constexpr int FM = TM / 64, FN = TN / 64;
   constexpr int kOffR = TM * kRowBytes;
-  la.issue(Lg, kt_copy, D);
-  lb.issue(Rg, kt_copy, D + kOffR);
+  la.issue(kt_copy, D);
+  lb.issue(kt_copy, D + kOffR);
   load_frags<FM, FN>(P, P + kOffR, fa, 0, fs.f0);
   load_frags<FM, FN>(P, P + kOffR, fa, 1, fs.f1);
   mma_frags<T, FM, FN>(fs.f2, acc);
@@ -393,18 +414,18 @@ __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, cons
   fa.init(wr, wc);
   DmaLoader<TM> la;
   DmaLoader<TN> lb;
-  la.init(ldl_bytes);
-  lb.init(ldr_bytes);
+  la.init(Lg, ldl_bytes);
+  lb.init(Rg, ldr_bytes);
 
   // Prologue: k-tiles kt0, kt0+1 (and kt0+2 with three stages), clamped,
   // into stages 0, 1 (and 2), then the MFMAs of substeps 0 and 1 of kt0.
-  la.issue(Lg, kt0, S::s0());
-  lb.issue(Rg, kt0, S::s0() + kOffR);
-  la.issue(Lg, clamp(kt0 + 1), S::s1());
-  lb.issue(Rg, clamp(kt0 + 1), S::s1() + kOffR);
+  la.issue(kt0, S::s0());
+  lb.issue(kt0, S::s0() + kOffR);
+  la.issue(clamp(kt0 + 1), S::s1());
+  lb.issue(clamp(kt0 + 1), S::s1() + kOffR);
   if constexpr (NS == 3) {
-    la.issue(Lg, clamp(kt0 + 2), S::s2());
-    lb.issue(Rg, clamp(kt0 + 2), S::s2() + kOffR);
+    la.issue(clamp(kt0 + 2), S::s2());
+    lb.issue(clamp(kt0 + 2), S::s2() + kOffR);
   }
   after_copies();
   // Loads complete in order: wait for the first k-tile only.
