@@ -70,10 +70,12 @@ typedef enum {
 
 /* Optional launch trace, for measuring kernels on the caller's stream.
  * Host memory owned by the caller.  When ns_options.trace is not NULL, each
- * launch whose kind bit is set in kind_mask is bracketed by two
- * hipEventRecord calls on the call's stream, using events[2*i] and
- * events[2*i+1] for the i-th recorded launch (i = count before the launch;
- * the caller creates the events), and kinds[i], flops[i] and bytes[i]
+ * launch whose kind bit is set in kind_mask is given events[2*i] and
+ * events[2*i+1] (i = count before the launch; the caller creates the events
+ * with timing enabled) as the start and stop events of hipExtLaunchKernel,
+ * so hipEventElapsedTime on the pair gives that kernel's run time.  Tracing
+ * leaves the GPU idle for a few microseconds around each recorded launch;
+ * kinds[i], flops[i] and bytes[i]
  * receive its kind, its algorithmic FLOPs (symmetric results counted at
  * half the dense cost; all matrices of a batch) and its algorithmic HBM
  * bytes (one read of each input and one write of each output).  count is

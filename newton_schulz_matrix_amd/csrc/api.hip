@@ -1,5 +1,6 @@
 // api.hip - host side of libnsortho: argument checks, workspace layout and
 // the launch sequence of both Newton-Schulz forms on the caller's stream.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -198,6 +199,23 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
 ns_status hip_status(hipError_t e) { return e == hipSuccess ? NS_OK : NS_ERR_HIP; }
 
 // Brackets launches with the caller's events when a trace is attached.
+// Start and stop events of one traced launch.  They are handed to
+// hipExtLaunchKernel, which binds them to the kernel's own dispatch: no
+// marker packets of their own go into the stream between kernels (two
+// hipEventRecord calls around a launch cost about 5 us of idle GPU each).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, LaunchEvents ev,
+                         Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  return hipGetLastError();
+}
+
+// Runs launch(LaunchEvents) for one kernel launch and records it in the
+// caller's trace when its kind is selected.
 struct Tracer {
   ns_trace* t;
   hipStream_t st;
@@ -206,11 +224,14 @@ struct Tracer {
     const bool rec = t && t->events && ((t->kind_mask >> (int)kind) & 1u) && t->count >= 0 &&
                      t->count < t->capacity;
     const int i = rec ? t->count : -1;
-    hipError_t e;
-    if (rec && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(t->events[2 * i]), st)) != hipSuccess) return e;
-    if ((e = launch()) != hipSuccess) return e;
+    LaunchEvents ev;
     if (rec) {
-      if ((e = hipEventRecord(reinterpret_cast<hipEvent_t>(t->events[2 * i + 1]), st)) != hipSuccess) return e;
+      ev.start = reinterpret_cast<hipEvent_t>(t->events[2 * i]);
+      ev.stop = reinterpret_cast<hipEvent_t>(t->events[2 * i + 1]);
+    }
+    hipError_t e;
+    if ((e = launch(ev)) != hipSuccess) return e;
+    if (rec) {
       if (t->kinds) t->kinds[i] = (int32_t)kind;
       if (t->flops) t->flops[i] = flops;
       if (t->bytes) t->bytes[i] = bytes;
@@ -242,50 +263,40 @@ bool use_pair(int edge, int esz, int64_t tiles) {
 }
 
 template <typename T, int TILE, bool GRAM_INPUT>
-hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s) {
+hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
   const int64_t ntri = (int64_t)a.tiles * (a.tiles + 1) / 2;
   const int ktiles = a.K / (kRowBytes / (int)sizeof(T));
+  const dim3 tiles_grid((unsigned)ntri, (unsigned)batch);
   a.batch = (int)batch;
   if constexpr (kHasPairKernels<T, TILE>) {
     if (use_pair(TILE, (int)sizeof(T), ntri * batch)) {
       if (use_persistent(TILE, ntri * batch, ktiles))
-        hipLaunchKernelGGL((k_sym_loop<T, TILE, GRAM_INPUT, 2>), dim3(2 * kPersistentGroups), dim3(kThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT, 2>), dim3((unsigned)ntri, (unsigned)batch), dim3(kThreads), 0,
-                           s, a);
-      return hipGetLastError();
+        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2>, dim3(2 * kPersistentGroups), dim3(kThreads), s, ev, a);
+      return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2>, tiles_grid, dim3(kThreads), s, ev, a);
     }
   }
   if constexpr (TILE <= 192) {
-    if (use_persistent(TILE, ntri * batch, ktiles)) {
-      hipLaunchKernelGGL((k_sym_loop<T, TILE, GRAM_INPUT>), dim3(kPersistentGroups), dim3(kThreads), 0, s, a);
-      return hipGetLastError();
-    }
+    if (use_persistent(TILE, ntri * batch, ktiles))
+      return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
   }
-  hipLaunchKernelGGL((k_sym<T, TILE, GRAM_INPUT>), dim3((unsigned)ntri, (unsigned)batch), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(k_sym<T, TILE, GRAM_INPUT>, tiles_grid, dim3(kThreads), s, ev, a);
 }
 
 template <typename T, typename OutT, int TILE>
-hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s) {
+hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+  constexpr int TN = nn_tile_n(TILE);
   const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
+  const dim3 flat((unsigned)(per * batch));
   a.batch = (int)batch;
   if constexpr (kHasPairKernels<T, TILE>) {
-    if (use_pair(TILE, (int)sizeof(T), per * batch)) {
-      hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE), 2>), dim3((unsigned)(per * batch)), dim3(kThreads), 0,
-                         s, a);
-      return hipGetLastError();
-    }
+    if (use_pair(TILE, (int)sizeof(T), per * batch))
+      return launch_kernel(k_nt<T, OutT, TILE, TN, 2>, flat, dim3(kThreads), s, ev, a);
   }
   if constexpr (TILE <= 192) {
-    if (use_persistent(TILE, per * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
-      hipLaunchKernelGGL((k_nt_loop<T, OutT, TILE, nn_tile_n(TILE)>), dim3(kPersistentGroups), dim3(kThreads), 0,
-                         s, a);
-      return hipGetLastError();
-    }
+    if (use_persistent(TILE, per * batch, a.K / (kRowBytes / (int)sizeof(T))))
+      return launch_kernel(k_nt_loop<T, OutT, TILE, TN>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
   }
-  hipLaunchKernelGGL((k_nt<T, OutT, TILE, nn_tile_n(TILE)>), dim3((unsigned)(per * batch)), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_kernel(k_nt<T, OutT, TILE, TN>, flat, dim3(kThreads), s, ev, a);
 }
 
 // One Newton-Schulz run over a batch, for internal type T and I/O type IO.
@@ -345,8 +356,8 @@ struct Runner {
     double bytes = (L == R ? 1.0 : 2.0) * n * inner * es + n * n * es * (1.0 + (E ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
     bytes *= bt;
     if (gram)
-      return tr.run(NS_KERNEL_GRAM, flops, bytes, [&] { return launch_sym<T, TILE, true>(a, p.batch, st); });
-    return tr.run(NS_KERNEL_SYM, flops, bytes, [&] { return launch_sym<T, TILE, false>(a, p.batch, st); });
+      return tr.run(NS_KERNEL_GRAM, flops, bytes, [&](LaunchEvents ev) { return launch_sym<T, TILE, true>(a, p.batch, st, ev); });
+    return tr.run(NS_KERNEL_SYM, flops, bytes, [&](LaunchEvents ev) { return launch_sym<T, TILE, false>(a, p.batch, st, ev); });
   }
 
   // Y = alpha * X_in + B X_in into X_out and X_out^T (E omitted when alpha
@@ -385,7 +396,7 @@ struct Runner {
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (3.0 + (with_e ? 1.0 : 0.0)));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
-                  [&] { return launch_nt<T, T, TILE>(a, p.batch, st); });
+                  [&](LaunchEvents ev) { return launch_nt<T, T, TILE>(a, p.batch, st, ev); });
   }
 
   // The caller's matrix = out_scale * (alpha * X_in + B X_in), oriented back.
@@ -423,7 +434,7 @@ struct Runner {
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (1.0 + (with_e ? 1.0 : 0.0)) + n * m * sizeof(IO));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
-                  [&] { return launch_nt<T, IO, TILE>(a, p.batch, st); });
+                  [&](LaunchEvents ev) { return launch_nt<T, IO, TILE>(a, p.batch, st, ev); });
   }
 
   hipError_t stage(float prescale, float eps) const {
@@ -432,22 +443,20 @@ struct Runner {
                         ((reinterpret_cast<uintptr_t>(user) & 15) == 0) &&
                         (p.batch == 1 || bstride % (16 / sizeof(IO)) == 0);
     const double elems = (double)p.rows * (double)p.cols * (double)p.batch;
-    hipError_t e = tr.run(NS_KERNEL_NORM, 0.0, elems * sizeof(IO), [&] {
-      hipLaunchKernelGGL((k_sumsq<IO>), dim3(p.partials, (unsigned)p.batch), dim3(kStageThreads), 0, st, user,
-                         p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, partial, p.partials);
-      return hipGetLastError();
+    hipError_t e = tr.run(NS_KERNEL_NORM, 0.0, elems * sizeof(IO), [&](LaunchEvents ev) {
+      return launch_kernel((k_sumsq<IO>), dim3(p.partials, (unsigned)p.batch), dim3(kStageThreads), st, ev,
+                           (const IO*)user, p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, partial, p.partials);
     });
     if (e != hipSuccess) return e;
     float* scales = reinterpret_cast<float*>(ws + p.off_scale);
     hipLaunchKernelGGL(k_scale, dim3((unsigned)p.batch), dim3(kStageThreads), 0, st, partial, p.partials, prescale,
                        eps, scales);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return tr.run(NS_KERNEL_STAGE, 0.0, elems * (sizeof(IO) + 2 * sizeof(T)), [&] {
+    return tr.run(NS_KERNEL_STAGE, 0.0, elems * (sizeof(IO) + 2 * sizeof(T)), [&](LaunchEvents ev) {
       const int bi = (int)(p.n_pad / 64), bj = (int)(p.m_pad / 64);
-      hipLaunchKernelGGL((k_stage_pair<IO, T>), dim3((unsigned)(bi * bj), (unsigned)p.batch), dim3(kStageThreads),
-                         0, st, user, p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, scales, xbuf(0), xtbuf(0),
-                         p.n_pad, p.m_pad, p.x_elems, p.transposed ? 1 : 0, bj);
-      return hipGetLastError();
+      return launch_kernel(k_stage_pair<IO, T>, dim3((unsigned)(bi * bj), (unsigned)p.batch), dim3(kStageThreads), st,
+                           ev, (const IO*)user, p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, (const float*)scales,
+                           xbuf(0), xtbuf(0), p.n_pad, p.m_pad, p.x_elems, p.transposed ? 1 : 0, bj);
     });
   }
 
@@ -646,11 +655,10 @@ struct MuonCall {
                         (reinterpret_cast<uintptr_t>(G) & 15) == 0 && (reinterpret_cast<uintptr_t>(M) & 15) == 0;
     const double elems = (double)p.rows * (double)p.cols * (double)p.batch;
     Tracer tr{opt ? opt->trace : nullptr, st};
-    hipError_t e = tr.run(NS_KERNEL_MOMENTUM, 0.0, elems * (2.0 * sizeof(IO) + 8.0), [&] {
-      hipLaunchKernelGGL((k_momentum<IO>), dim3((unsigned)p.rows, (unsigned)p.batch), dim3(kStageThreads), 0, st,
-                         reinterpret_cast<const IO*>(G), M, reinterpret_cast<IO*>(U), p.cols, ld, bstride,
-                         vec_ok ? 1 : 0, mu, nesterov ? 1 : 0);
-      return hipGetLastError();
+    hipError_t e = tr.run(NS_KERNEL_MOMENTUM, 0.0, elems * (2.0 * sizeof(IO) + 8.0), [&](LaunchEvents ev) {
+      return launch_kernel(k_momentum<IO>, dim3((unsigned)p.rows, (unsigned)p.batch), dim3(kStageThreads), st, ev,
+                           reinterpret_cast<const IO*>(G), M, reinterpret_cast<IO*>(U), p.cols, ld, bstride,
+                           vec_ok ? 1 : 0, mu, nesterov ? 1 : 0);
     });
     if (e != hipSuccess) return NS_ERR_HIP;
     return run_typed<T, IO>(p, IoSpec{U, p.cols, p.rows * p.cols, W, ld, bstride, true, -lr}, steps, a, b, c, opt, ws,
