@@ -67,6 +67,10 @@ def parse():
                              "moe-experts", "moe-experts-t", "small-fp32",
                              "nanogpt-set", "root-split", "muon-step",
                              "copy-calibration"])
+    ap.add_argument("--shape", type=int, nargs=2, default=None,
+                    metavar=("ROWS", "COLS"),
+                    help="one ROWS x COLS column-scaled bf16 matrix instead "
+                         "of --workload")
     ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
     ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
     ap.add_argument("--restart-mask", type=int, default=1 << 4)
@@ -78,7 +82,7 @@ def parse():
     return ap.parse_args()
 
 
-def workload_input(name):
+def workload_input(name, shape=None):
     """(list of host input tensors, I/O dtype name, step kind).
 
     The kind is "ns" (orthogonalize each input), "root" (ROOT split, then
@@ -87,6 +91,8 @@ def workload_input(name):
     several tensors is run as one call each, in order, per step.
     """
     import workloads
+    if shape is not None:
+        return [workloads.column_scaled(shape[0], shape[1], seed=3)], "bf16", "ns"
     if name == "llama8b-mlp":
         return [workloads.llama8b((4096, 14336))], "bf16", "ns"
     if name == "llama8b-down":
@@ -384,7 +390,9 @@ def main():
     from newton_schulz_matrix_amd.flops import ns_flops
 
     dev = torch.device("cuda:0")
-    host_inputs, io, kind = workload_input(args.workload)
+    if args.shape is not None:
+        args.workload = f"column-scaled-{args.shape[0]}x{args.shape[1]}"
+    host_inputs, io, kind = workload_input(args.workload, args.shape)
     inputs = [m.to(dev) for m in host_inputs]
     shapes = [(m.shape[0] if m.dim() == 3 else 1, m.shape[-2], m.shape[-1])
               for m in host_inputs]
