@@ -333,10 +333,12 @@ struct Runner {
   T* nnbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_nn[i]); }
 
   // C = beta*E + gamma * L R^T on upper tiles, mirrored.  L and R are the
-  // X buffers (K = m_pad) or n x n buffers (K = n_pad).
+  // X buffers (K = m_pad) or n x n buffers (K = n_pad).  E is null or L
+  // (the kernels take E's tile from L's k-tiles).
   template <int TILE>
   hipError_t sym(const T* L, const T* R, int K, int ldk, const T* E, float beta, float gamma, T* C, T* C2,
                  float delta) const {
+    if (E && E != L) return hipErrorInvalidValue;
     SymArgs<T> a;
     a.L = L;
     a.R = R;
@@ -520,16 +522,19 @@ struct Runner {
       // Z' = b R + c R^2; at a fresh start Q = a I + Z' comes out of the same
       // epilogue.
       if ((e = sym<TILE>(R, R, kn, np, R, bk, ck, Z, fresh ? Qb[qi] : nullptr, ak)) != hipSuccess) return e;
+      // The products below are taken as Q Z', R Z' and V Z' (equal to Z' Q,
+      // Z' R and Z' V: all are polynomials in the same Gram matrix), so that
+      // the epilogue's E operand is the left operand.
       if (!fresh) {
-        if ((e = sym<TILE>(Z, Qb[qi], kn, np, Qb[qi], ak, 1.f, Qb[qi ^ 1], nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(Qb[qi], Z, kn, np, Qb[qi], ak, 1.f, Qb[qi ^ 1], nullptr, 0.f)) != hipSuccess) return e;
         qi ^= 1;
       }
       fresh = false;
       const bool need_r = k < steps && !((mask >> (k + 1)) & 1u);
       if (need_r) {
         T* V = Qb[qi ^ 1];
-        if ((e = sym<TILE>(Z, R, kn, np, R, ak, 1.f, V, nullptr, 0.f)) != hipSuccess) return e;
-        if ((e = sym<TILE>(Z, V, kn, np, V, ak, 1.f, R, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(R, Z, kn, np, R, ak, 1.f, V, nullptr, 0.f)) != hipSuccess) return e;
+        if ((e = sym<TILE>(V, Z, kn, np, V, ak, 1.f, R, nullptr, 0.f)) != hipSuccess) return e;
       }
     }
     return nn_final<TILE>(Qb[qi], xi, false, 0.f, unscale);

@@ -356,11 +356,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int TM, int TN, int G>
+template <typename T, int TM, int TN, int G, class Capture>
 __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const DmaLoader<TM>& la,
-                                          const DmaLoader<TN>& lb, int kt_copy, char* __restrict__ D,
+                                          const DmaLoader<TN>& lb, int kt_copy, int kt_read, char* __restrict__ D,
                                           const char* __restrict__ P, const FragAddr& fa,
-                                          FragSets<TM / 64, TN / 64>& fs, f32x16 (&acc)[TM / 64][TN / 64]) {
+                                          FragSets<TM / 64, TN / 64>& fs, f32x16 (&acc)[TM / 64][TN / 64],
+                                          Capture&& capture) {
   constexpr int FM = TM / 64, FN = TN / 64;
   constexpr int kOffR = TM * kRowBytes;
   la.issue(kt_copy, D);
@@ -374,6 +375,9 @@ __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const 
   mma_frags<T, FM, FN>(fs.f0, acc);
   mma_frags<T, FM, FN>(fs.f1, acc);
   schedule_step<T, TM, TN, G>();
+  // Extra LDS reads of k-tile kt_read (stage P) for the caller; the wait
+  // below completes them before the next step's copies overwrite P.
+  capture(kt_read, P, fa);
   // With three stages the copy just issued may stay in flight (it lands in
   // a stage read two steps later); the one issued a step ago must be
   // complete.
@@ -390,11 +394,14 @@ __device__ __forceinline__ void pipe_step(const char* Lg, const char* Rg, const 
 // `after_copies` runs right after the prologue's copies are issued and
 // issues `extra_loads` more vector-memory loads per thread (the epilogue
 // operand's prefetch, 0 when there is none); the first wait counts them, so
-// they do not delay the first k-tile.
-template <typename T, int TM, int TN, int kExtraLoads, int G, class AfterCopies>
+// they do not delay the first k-tile.  capture(kt, sL, fa) runs once per
+// k-tile while k-tile kt is in LDS, with sL the L operand's base in its
+// stage and fa the wave's fragment-row offsets; its LDS reads complete
+// before the stage is reused.
+template <typename T, int TM, int TN, int kExtraLoads, int G, class AfterCopies, class Capture>
 __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, const char* Rg, int64_t ldr_bytes,
                                          int kt0, int kt1, Acc<T, TM, TN>& acc, bool extra_loads,
-                                         AfterCopies&& after_copies) {
+                                         AfterCopies&& after_copies, Capture&& capture) {
   constexpr int FM = TM / 64, FN = TN / 64;
   constexpr int kOffR = TM * kRowBytes;
   constexpr int kDma = TM / 32 + TN / 32;  // copy instructions per k-tile per wave
@@ -445,6 +452,7 @@ __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, cons
   }
   mma_frags<T, FM, FN>(fs.f0, acc.v);
   mma_frags<T, FM, FN>(fs.f1, acc.v);
+  capture(kt0, S::s0(), fa);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NS - 2) * kDma));
   lds_barrier();
 
@@ -453,7 +461,7 @@ __device__ __forceinline__ void mainloop(const char* Lg, int64_t ldl_bytes, cons
   // three so that every step names its stages directly (the compiler then
   // sees that a step's reads and its copies touch different objects).
   auto step = [&](int t, char* D, const char* P) {
-    pipe_step<T, TM, TN, G>(Lg, Rg, la, lb, clamp(t + NS), D, P, fa, fs, acc.v);
+    pipe_step<T, TM, TN, G>(Lg, Rg, la, lb, clamp(t + NS), t + 1, D, P, fa, fs, acc.v, capture);
   };
   if constexpr (NS == 3) {
     int t = kt0;
@@ -485,7 +493,7 @@ template <typename T>
 struct SymArgs {
   const T* L;        // n x K, row stride ldk
   const T* R;        // n x K, row stride ldk
-  const T* E;        // n x n (ldn) or null when beta == 0
+  const T* E;        // null when beta == 0, else L itself (ldn == ldk)
   T* C;              // n x n (ldn)
   T* C2;             // optional second output: C + delta * I on rows < n_real
   int64_t sL, sR, sE, sC, sC2;  // batch strides in elements
@@ -653,10 +661,13 @@ __device__ __forceinline__ void acc_zero(Acc<T, TM, TN>& acc) {
 // The epilogue's E operand (the "alpha E +" / "beta E +" term) in the
 // accumulator layout: lane (lr, h) of wave (wr, wc) needs E[il][jl..jl+3]
 // for il = wr + 32 fm + lr, jl = wc + 32 fn + 8 g + 4 h.  Tiles up to 192
-// have the registers to load it (8 bytes per (fm, fn, g)) before the main
-// loop, so its latency and its burst of HBM reads overlap the MFMAs instead
-// of sitting between the last MFMA and the stores; the 256 tile loads it in
-// the epilogue.
+// have the registers to hold it (8 bytes per (fm, fn, g)) through the main
+// loop, so it never sits between the last MFMA and the stores; the 256 tile
+// loads it in the epilogue.  The update loads it from global memory before
+// the main loop (load); the symmetric products, where E is the L operand,
+// take it from L's k-tiles col0 / 64 .. (col0 + TN) / 64 while they are in
+// LDS (capture), so it costs no HBM reads and does not hold up the first
+// k-tile.
 template <typename T, int TM, int TN>
 struct EPrefetch {
   static constexpr int FM = TM / 64, FN = TN / 64;
@@ -677,6 +688,44 @@ struct EPrefetch {
           for (int g = 0; g < 4; ++g)
             v[fm][fn][g] = *reinterpret_cast<const uint2*>(E + (row0 + wr + fm * 32 + lr) * ld + col0 + wc +
                                                            fn * 32 + 8 * g + 4 * h);
+    }
+  }
+  // E = L: from the L operand's k-tile kt in LDS (base sL, rows of the tile
+  // at kRowBytes each), if kt holds some of this thread's columns.  kb is
+  // the first k-tile of the tile's column block (col0 / 64 for 16-bit T).
+  __device__ __forceinline__ void zero() {
+    if constexpr (kEnabled) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) v[fm][fn][g] = uint2{0u, 0u};
+    }
+  }
+  // Row il = wr + 32 fm + lr sits at fa.row0L + 32 fm kRowBytes with the
+  // chunk swizzle fa.swL0 / fa.swL1 (even / odd fm), as for the fragment
+  // reads.
+  __device__ __forceinline__ void capture(int kt, const char* sL, int kb, const FragAddr& fa) {
+    if constexpr (kEnabled) {
+      const int d = kt - kb;
+      if (d < 0 || d >= TN / 64) return;
+      const int w = threadIdx.x >> 6, h = (threadIdx.x & 63) >> 5;
+      const int wc = (w & 1) * (TN / 2);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int jd = wc + fn * 32 + 8 * g - 64 * d;  // column inside k-tile kt (uniform per wave)
+          if (jd < 0 || jd >= 64) continue;
+          const int c = jd >> 3;
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            const int sw = (fm & 1) ? fa.swL1 : fa.swL0;
+            v[fm][fn][g] = *reinterpret_cast<const uint2*>(sL + fa.row0L + fm * 32 * kRowBytes + ((c ^ sw) << 4) +
+                                                           8 * h);
+          }
+        }
     }
   }
   // E[il][jl..jl+3] as floats: from the registers, or loaded now.
@@ -706,12 +755,18 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
   const bool diag_tile = (tm == tn);
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
+  // E is null or the L operand (SymArgs), so its tile rows are L's tile
+  // rows and its columns col0.. are L's k-tiles from col0 / BK on.
   using EP = EPrefetch<T, TILE, TILE>;
   EP ep;
+  ep.zero();
   A acc;
   acc_zero(acc);
-  mainloop<T, TILE, TILE, EP::kLoads, G>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
-                                      [&] { ep.load(E, p.ldn, row0, col0); });
+  const int kb = (int)(col0 / BK);
+  mainloop<T, TILE, TILE, 0, G>(Lg, ldk_bytes, Rg, ldk_bytes, 0, p.K / BK, acc, false, [] {},
+                                [&](int kt, const char* sL, const FragAddr& fa) {
+                                  if (E) ep.capture(kt, sL, kb, fa);
+                                });
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
@@ -865,7 +920,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   A acc;
   acc_zero(acc);
   mainloop<T, TM, TN, EP::kLoads, G>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
-                                  [&] { ep.load(E, p.lde, row0, col0); });
+                                  [&] { ep.load(E, p.lde, row0, col0); }, [](int, const char*, const FragAddr&) {});
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
