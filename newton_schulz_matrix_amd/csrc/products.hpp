@@ -280,6 +280,10 @@ template <> struct StageMem<32768> {
 
 constexpr int kLdsBytes = 160 * 1024;
 
+// C2's diagonal of a diagonal tile (up to 256 elements of up to 4 bytes),
+// rounded once from fp32 in phase A and merged into the row stores.
+__shared__ __attribute__((aligned(16))) char g_c2_diag[1024];
+
 // G is the number of work-groups a kernel is built to share a compute unit
 // with: G = 2 takes two stages (two 128-tile work-groups then fit in LDS
 // together, and one's start-up and epilogue overlap the other's main loop).
@@ -740,6 +744,42 @@ struct EPrefetch {
   }
 };
 
+// A 16-byte chunk of T elements with elements k < e taken from `lo` and the
+// others from `up` (word masks, so the chunks stay in registers).
+template <typename T>
+__device__ __forceinline__ uint4 merge_below(uint4 lo, uint4 up, int e) {
+  const uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w}, u[4] = {up.x, up.y, up.z, up.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t m;
+    if constexpr (sizeof(T) == 2)
+      m = (2 * i < e ? 0x0000ffffu : 0u) | (2 * i + 1 < e ? 0xffff0000u : 0u);
+    else
+      m = i < e ? 0xffffffffu : 0u;
+    o[i] = (l[i] & m) | (u[i] & ~m);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
+// The chunk v with element k replaced by d.
+template <typename T>
+__device__ __forceinline__ uint4 with_elem(uint4 v, int k, T d) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t bits = __builtin_bit_cast(uint16_t, d);
+      const uint32_t lo = 2 * i == k ? bits : (w[i] & 0xffffu);
+      const uint32_t hi = 2 * i + 1 == k ? bits : (w[i] >> 16);
+      w[i] = lo | (hi << 16);
+    } else {
+      if (i == k) w[i] = __builtin_bit_cast(uint32_t, d);
+    }
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
 // One upper-triangle tile (tm <= tn) of matrix bz of a symmetric product.
 template <typename T, int TILE, int G>
 __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, int bz) {
@@ -754,6 +794,8 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
   T* C = p.C + bz * p.sC;
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
   const bool diag_tile = (tm == tn);
+  static_assert(TILE * sizeof(T) <= sizeof(g_c2_diag), "C2 diagonal buffer");
+  T* c2d = reinterpret_cast<T*>(g_c2_diag);
   const int64_t row0 = (int64_t)tm * TILE, col0 = (int64_t)tn * TILE;
   // E is null or the L operand (SymArgs), so its tile rows are L's tile
   // rows and its columns col0.. are L's k-tiles from col0 / BK on.
@@ -793,75 +835,65 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
         if (C2 && diag_tile) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (il == jl + e && row0 + il < p.n_real)
-              C2[(row0 + il) * p.ldn + col0 + il] = from_f32<T>(v[e] + p.delta);
+            if (il == jl + e) c2d[il] = from_f32<T>(v[e] + p.delta);
         }
       }
     }
   }
   __syncthreads();
 
-  // Phase B: rows of the tile.  On a diagonal tile each element (r, j) is
-  // taken from the upper triangle, tile[min(r, j)][max(r, j)], so the result
-  // is exactly symmetric; C2's diagonal was written in phase A.  Every
-  // thread handles the same number of chunks, so the off-diagonal loop is
-  // unrolled and its LDS reads overlap.
   constexpr int kChunks = TILE * TL::kCPR;
   constexpr int EC = TL::kEC;
+  constexpr int kB = TL::kCPR;  // EC x EC blocks along a tile edge
+  constexpr int kBlocks = kB * kB;
   static_assert(kChunks % kThreads == 0, "whole chunks per thread");
-  if (!diag_tile) {
+  // Phase B: rows of the tile.  Every thread handles the same number of
+  // chunks, so the loop is unrolled and its LDS reads overlap.  A diagonal
+  // tile takes every element from its upper triangle, so the stored matrix
+  // is exactly symmetric: here it writes only the chunks right of its
+  // diagonal blocks, and phase C the rest.
 #pragma unroll 6
-    for (int it = 0; it < kChunks / kThreads; ++it) {
-      const int q = it * kThreads + threadIdx.x;
-      const int r = q / TL::kCPR, c = q % TL::kCPR;
+  for (int it = 0; it < kChunks / kThreads; ++it) {
+    const int q = it * kThreads + threadIdx.x;
+    const int r = q / TL::kCPR, c = q % TL::kCPR;
+    if (!diag_tile || c > r / EC) {
       const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
       *reinterpret_cast<uint4*>(C + (row0 + r) * p.ldn + col0 + c * EC) = val;
       if (C2) *reinterpret_cast<uint4*>(C2 + (row0 + r) * p.ldn + col0 + c * EC) = val;
     }
-  } else {
-    for (int q = threadIdx.x; q < kChunks; q += kThreads) {
-      const int r = q / TL::kCPR, c = q % TL::kCPR;
-      T* dst = C + (row0 + r) * p.ldn + col0 + c * EC;
-      T vals[EC];
-#pragma unroll
-      for (int e = 0; e < EC; ++e) {
-        const int j = c * EC + e;
-        vals[e] = *reinterpret_cast<const T*>(j >= r ? TL::at(r, j) : TL::at(j, r));
-      }
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
-      if (C2) {
-        T* dst2 = C2 + (row0 + r) * p.ldn + col0 + c * EC;
-        const int jd = r - c * EC;  // position of the diagonal inside this chunk
-        if (jd >= 0 && jd < EC && row0 + r < p.n_real) {
-#pragma unroll
-          for (int e = 0; e < EC; ++e)
-            if (e != jd) dst2[e] = vals[e];
-        } else {
-          *reinterpret_cast<uint4*>(dst2) = *reinterpret_cast<const uint4*>(vals);
-        }
-      }
-    }
-    return;
   }
 
   // Phase C: the mirrored tile, C[col0 + j][row0 + i] = tile[i][j], from
   // EC x EC blocks transposed in registers.  Block (rb, cb) gives chunk rb of
   // mirrored rows cb*EC .. cb*EC + EC - 1; consecutive threads take
-  // consecutive rb, so each mirrored row is written as adjacent chunks.
-  constexpr int kB = TL::kCPR;  // blocks along a tile edge
-  constexpr int kBlocks = kB * kB;
+  // consecutive rb, so each mirrored row is written as adjacent chunks.  On
+  // a diagonal tile the mirror of each upper block (rb < cb) is the lower
+  // block (cb, rb); a diagonal block (rb == cb) is written once, its row e
+  // taking the elements left of the diagonal from its transpose and the
+  // rest as staged, and C2's copy takes the diagonal element from phase A
+  // (real rows).  Blocks below the diagonal are not read.
 #pragma unroll 1
   for (int it = 0; it < (kBlocks + kThreads - 1) / kThreads; ++it) {
     const int q = it * kThreads + threadIdx.x;
-    if (kBlocks % kThreads == 0 || q < kBlocks) {
-      const int rb = q % kB, cb = q / kB;
+    const int rb = q % kB, cb = q / kB;
+    if ((kBlocks % kThreads == 0 || q < kBlocks) && !(diag_tile && rb > cb)) {
       uint4 cols[EC];
       TL::block_t(rb, cb, cols);
+      const bool on_diag = diag_tile && rb == cb;
+      if (on_diag) {
+#pragma unroll
+        for (int e = 0; e < EC; ++e)
+          cols[e] = merge_below<T>(cols[e], *reinterpret_cast<const uint4*>(TL::chunk(rb * EC + e, cb)), e);
+      }
 #pragma unroll
       for (int e = 0; e < EC; ++e) {
         const int64_t off = (col0 + cb * EC + e) * p.ldn + row0 + rb * EC;
         *reinterpret_cast<uint4*>(C + off) = cols[e];
-        if (C2) *reinterpret_cast<uint4*>(C2 + off) = cols[e];
+        if (C2) {
+          const int rr = rb * EC + e;
+          *reinterpret_cast<uint4*>(C2 + off) =
+              on_diag && row0 + rr < p.n_real ? with_elem<T>(cols[e], e, c2d[rr]) : cols[e];
+        }
       }
     }
   }
