@@ -71,6 +71,13 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
+// The smallest magnitude that rounds to infinity (round to nearest even):
+// a value is finite after rounding to T exactly when its magnitude is below
+// this (NaN compares false).
+template <typename T> constexpr float kRoundsToInf = __builtin_inff();
+template <> constexpr float kRoundsToInf<_Float16> = 65520.0f;            // 65504 + half an ulp
+template <> constexpr float kRoundsToInf<__bf16> = 0x1.ffp127f;          // bf16 max + half an ulp
+
 // Four consecutive elements <-> four floats.
 template <typename T> struct Quad;
 template <> struct Quad<float> {
@@ -993,9 +1000,9 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
         v[3] = p.gamma * acc.v[fm][fn][4 * g + 3];
         if (E) v += p.alpha * ep.get(E, p.lde, row0, col0, il, jl, fm, fn, g);
         v *= scale;
-        if (p.final_out) {
+        if (p.final_out && p.d_status) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bad |= !__builtin_isfinite(to_f32<OutT>(from_f32<OutT>(v[e])));
+          for (int e = 0; e < 4; ++e) bad |= !(fabsf(v[e]) < kRoundsToInf<OutT>);
         }
         Quad<OutT>::store(reinterpret_cast<OutT*>(TL::at(il, jl)), v);
       }
