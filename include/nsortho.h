@@ -189,7 +189,8 @@ ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows,
  *            bytes, 256-byte aligned.
  * B is rounded to `dtype` (clipped entries become lambda rounded to nearest
  * even); O is computed as M - B in fp32 and rounded.  NaN inputs pass
- * through to B.  numel >= 1.
+ * through to B.  1 <= numel <= 2^32 - 1 (the select's bin counts are
+ * 32-bit); otherwise NS_ERR_INVALID_ARG, and the workspace query returns 0.
  */
 size_t ns_soft_threshold_workspace_size(int64_t numel, ns_dtype dtype);
 

@@ -702,8 +702,10 @@ ns_status muon_impl(void* W, const void* G, float* M, int64_t batch, int64_t row
                                     reinterpret_cast<hipStream_t>(stream)});
 }
 
-// Soft-threshold workspace: select state + three histograms.
-size_t threshold_ws_bytes() { return align_up(sizeof(SelectState)) + align_up(3 * kHistBins * sizeof(uint32_t)); }
+// Soft-threshold workspace: select state + three histograms (kHistCopies copies each).
+size_t threshold_ws_bytes() {
+  return align_up(sizeof(SelectState)) + align_up(3 * kHistCopies * kHistBins * sizeof(uint32_t));
+}
 
 template <typename IO>
 ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float lambda, float mult,
@@ -714,8 +716,16 @@ ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float 
   const IO* m = reinterpret_cast<const IO*>(M);
   const int64_t blocks64 = (numel + 255) / 256;
   const unsigned grid = (unsigned)(blocks64 < 2048 ? blocks64 : 2048);
+  // Histogram passes: about 64 elements per thread, so that fewer blocks
+  // merge their LDS histograms into the global one.
+  const int64_t hblocks = (numel + (int64_t)kHistThreads * 64 - 1) / ((int64_t)kHistThreads * 64);
+  const unsigned hgrid = (unsigned)(hblocks < 512 ? hblocks : 512);
+  const int vec_hist = (reinterpret_cast<uintptr_t>(M) & 15) == 0 ? 1 : 0;
+  const int vec_clip = vec_hist && (reinterpret_cast<uintptr_t>(B) & 15) == 0 &&
+                       (!O || (reinterpret_cast<uintptr_t>(O) & 15) == 0) ? 1 : 0;
   const uint64_t rank = (uint64_t)((numel + 1) / 2);
-  hipLaunchKernelGGL(k_select_init, dim3((3 * kHistBins + 255) / 256), dim3(256), 0, st, state, hist, 3 * kHistBins,
+  hipLaunchKernelGGL(k_select_init, dim3((3 * kHistCopies * kHistBins + 255) / 256), dim3(256), 0, st, state, hist,
+                     3 * kHistCopies * kHistBins,
                      rank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return NS_ERR_HIP;
@@ -734,15 +744,15 @@ ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float 
       ++npass;
     }
     for (int ps = 0; ps < npass; ++ps) {
-      uint32_t* h = hist + ps * kHistBins;
-      hipLaunchKernelGGL((k_radix_hist<IO>), dim3(grid), dim3(kHistThreads), 0, st, m, numel, state, shifts[ps],
-                         bits[ps], h);
+      uint32_t* h = hist + ps * kHistCopies * kHistBins;
+      hipLaunchKernelGGL((k_radix_hist<IO>), dim3(hgrid), dim3(kHistThreads), 0, st, m, numel, state, shifts[ps],
+                         bits[ps], h, vec_hist);
       hipLaunchKernelGGL((k_radix_pick<IO>), dim3(1), dim3(kHistThreads), 0, st, state, h, shifts[ps], bits[ps],
                          ps == npass - 1 ? 1 : 0, mult, -1.f, d_lambda_out);
     }
   }
   hipLaunchKernelGGL((k_clip_split<IO>), dim3(grid), dim3(256), 0, st, m, reinterpret_cast<IO*>(B),
-                     reinterpret_cast<IO*>(O), numel, state);
+                     reinterpret_cast<IO*>(O), numel, state, vec_clip);
   return hip_status(hipGetLastError());
 }
 
@@ -797,8 +807,11 @@ ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch, int64_t 
                    nesterov, steps, a, b, c, mode, opt, workspace, workspace_bytes, stream);
 }
 
+// Bin counts are 32-bit: at most 2^32 - 1 elements.
+constexpr int64_t kMaxThresholdNumel = (int64_t(1) << 32) - 1;
+
 size_t ns_soft_threshold_workspace_size(int64_t numel, ns_dtype dtype) {
-  if (numel < 1) return 0;
+  if (numel < 1 || numel > kMaxThresholdNumel) return 0;
   if (dtype != NS_BF16 && dtype != NS_FP16 && dtype != NS_FP32) return 0;
   return threshold_ws_bytes();
 }
@@ -806,7 +819,7 @@ size_t ns_soft_threshold_workspace_size(int64_t numel, ns_dtype dtype) {
 ns_status ns_soft_threshold_split(const void* M, void* B, void* O, int64_t numel, ns_dtype dtype, float lambda,
                                   float mult, float* d_lambda_out, void* workspace, size_t workspace_bytes,
                                   ns_stream_t stream) {
-  if (!M || !B || numel < 1) return NS_ERR_INVALID_ARG;
+  if (!M || !B || numel < 1 || numel > kMaxThresholdNumel) return NS_ERR_INVALID_ARG;
   if (isnan(lambda) || (lambda < 0.f && !(isfinite(mult) && mult >= 0.f))) return NS_ERR_INVALID_ARG;
   if (dtype != NS_BF16 && dtype != NS_FP16 && dtype != NS_FP32) return NS_ERR_UNSUPPORTED_DTYPE;
   if (!workspace || workspace_bytes < threshold_ws_bytes() || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)

@@ -215,6 +215,10 @@ def test_soft_threshold_argument_checks():
             None, ctypes.c_void_p(a["ws"]), a["wsb"], None)
     assert call(M=0) == 1
     assert call(numel=0) == 1
+    # Bin counts are 32-bit: 2^32 elements and more are refused.
+    assert lib.ns_soft_threshold_workspace_size(1 << 32, 0) == 0
+    assert lib.ns_soft_threshold_workspace_size((1 << 32) - 1, 0) == need
+    assert call(numel=1 << 32) == 1
     assert call(lam=float("nan")) == 1
     assert call(mult=float("inf")) == 1
     assert call(dt=4) == 2

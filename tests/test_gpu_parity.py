@@ -318,3 +318,38 @@ def test_soft_threshold_explicit_lambda_and_in_place():
     assert np.array_equal(x.double().cpu().numpy(), ref_b)
     assert np.abs(o.double().cpu().numpy() - ref_o).max() <= 2 ** -7 * (
         np.abs(ref_o).max() + 1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_soft_threshold_unaligned_and_ragged(dtype):
+    # A contiguous view that starts 3 elements into its buffer (not 16-byte
+    # aligned) and has a ragged length takes the element-by-element paths;
+    # the same values in an aligned buffer take the 16-byte ones.  The split
+    # is elementwise and the median exact, so both agree bit for bit, and
+    # with the oracle as in the test above.
+    dev = _dev()
+    numel = 100_003
+    m = workloads.student_t((numel,), seed=31, dtype=dtype)
+    torch_dtype = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    buf = torch.zeros(numel + 3, dtype=torch_dtype, device=dev)
+    buf[3:] = m.to(dev)
+    view = buf[3:]
+    assert view.is_contiguous() and view.data_ptr() % 16 != 0
+    lam_u = torch.zeros(1, dtype=torch.float32, device=dev)
+    lam_a = torch.zeros(1, dtype=torch.float32, device=dev)
+    b_u, o_u = nsa.soft_threshold_split(view, lambda_out=lam_u)
+    aligned = m.to(dev)
+    assert aligned.data_ptr() % 16 == 0
+    b_a, o_a = nsa.soft_threshold_split(aligned, lambda_out=lam_a)
+    torch.cuda.synchronize()
+    assert lam_u.item() == lam_a.item()
+    assert torch.equal(b_u, b_a) and torch.equal(o_u, o_a)
+    m64 = m.double().numpy()
+    assert lam_a.item() == pytest.approx(3.0 * oracle.lower_median_abs(m64), rel=1e-7)
+    b_ref, _, lam_ref = oracle.soft_threshold_split(m64)
+    clipped = np.abs(m64) > lam_ref
+    assert np.array_equal(b_a.double().cpu().numpy()[~clipped], m64[~clipped])
+    # Without the outlier output (O null) the robust part is the same.
+    b_n, o_n = nsa.soft_threshold_split(aligned.clone(), outliers=False)
+    torch.cuda.synchronize()
+    assert o_n is None and torch.equal(b_n, b_a)
