@@ -10,7 +10,8 @@ products are dense, so the work does not depend on the values.
 
 Other workloads (--workload): the transposed and square Llama shapes, the
 MoE expert batch (128 x 2048 x 1408 and transposed), the NanoGPT-124M
-weight set (three batched calls per step), the ROOT split of a 2048 x 8192
+weight set (three batched calls per step, each on a stream of its own
+unless --serial), the ROOT split of a 2048 x 8192
 Student-t gradient followed by orthogonalization of its robust part, and a
 256 x 1024 fp32 matrix, and a whole Muon step (momentum, orthogonalization,
 weight update) with the 4096 x 14336 matrix as the gradient.  `value`
@@ -76,6 +77,9 @@ def parse():
     ap.add_argument("--restart-mask", type=int, default=1 << 4)
     ap.add_argument("--tile", type=int, default=0, choices=[0, 128, 192, 256],
                     help="force the products' tile edge (0: automatic)")
+    ap.add_argument("--serial", action="store_true",
+                    help="run a multi-call step's calls one after another on "
+                         "one stream (default: one stream per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-form companion measurement")
@@ -205,16 +209,39 @@ def make_step(inputs, mode, args, kind):
                      torch.zeros(x.shape, dtype=torch.float32, device=x.device))
         calls.append((fn, x, kw, extra))
 
+    # Calls on different inputs are independent: with several, each gets a
+    # stream of its own (default priority), forked from and joined back into
+    # the caller's stream, so one call's short launches overlap another's.
+    streams = ([torch.cuda.Stream(device=inputs[0].device) for _ in calls]
+               if len(calls) > 1 and not args.serial else None)
+
     def step(trace=None):
-        for fn, x, kw, extra in calls:
-            tkw = dict(kw) if trace is None else dict(kw, trace=trace)
-            if kind == "muon":
-                w, m = extra
-                nsa.muon_step(w, x, m, 0.02, 0.95, True, **tkw)
-                continue
-            if kind == "root":
-                nsa.soft_threshold_split(extra, out_b=x)
-            fn(x, **tkw)
+        if streams is None:
+            run_calls(trace, [None] * len(calls))
+            return
+        main = torch.cuda.current_stream()
+        for s in streams:
+            s.wait_stream(main)
+        run_calls(trace, streams)
+        for s in streams:
+            main.wait_stream(s)
+
+    def run_calls(trace, call_streams):
+        import contextlib
+        for (fn, x, kw, extra), s in zip(calls, call_streams):
+            ctx = torch.cuda.stream(s) if s is not None else contextlib.nullcontext()
+            with ctx:
+                one_call(fn, x, kw, extra, trace)
+
+    def one_call(fn, x, kw, extra, trace):
+        tkw = dict(kw) if trace is None else dict(kw, trace=trace)
+        if kind == "muon":
+            w, m = extra
+            nsa.muon_step(w, x, m, 0.02, 0.95, True, **tkw)
+            return
+        if kind == "root":
+            nsa.soft_threshold_split(extra, out_b=x)
+        fn(x, **tkw)
     return step
 
 
@@ -465,6 +492,7 @@ def main():
                    "ns_steps": 5, "abc": list(nsa.TUNED_ABC),
                    "restart_mask": args.restart_mask,
                    "tile": args.tile or "auto",
+                   "streams": len(inputs) if len(inputs) > 1 and not args.serial else 1,
                    "parallelism": "single-gpu"},
         "tflops": tflops,
         "mfma_frac": tflops / PEAK_TFLOPS[dtype],

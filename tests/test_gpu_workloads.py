@@ -101,6 +101,32 @@ def test_nanogpt_weight_set():
                 assert err < 1e-2
 
 
+def test_nanogpt_groups_on_concurrent_streams():
+    # The three weight groups as the bench runs them: one batched call per
+    # group, each on its own stream with its own workspace, launched back to
+    # back so their kernels overlap.  The library keeps no state between
+    # calls, so the results equal one-at-a-time calls bit for bit.
+    dev = _dev()
+    groups = [torch.stack(m) for m in workloads.nanogpt_set().values()]
+    serial = [g.to(dev) for g in groups]
+    for x in serial:
+        nsa.orthogonalize_batched(x, mode="gram")
+    torch.cuda.synchronize()
+    conc = [g.to(dev) for g in groups]
+    streams = [torch.cuda.Stream() for _ in conc]
+    main = torch.cuda.current_stream()
+    for s in streams:
+        s.wait_stream(main)
+    for x, s in zip(conc, streams):
+        with torch.cuda.stream(s):
+            nsa.orthogonalize_batched(x, mode="gram")
+    for s in streams:
+        main.wait_stream(s)
+    torch.cuda.synchronize()
+    for a, b in zip(serial, conc):
+        assert torch.equal(a, b)
+
+
 def test_root_split_then_orthogonalize():
     dev = _dev()
     m = workloads.heavy_tailed()
