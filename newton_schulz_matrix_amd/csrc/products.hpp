@@ -717,9 +717,8 @@ struct EPrefetch {
                                                            fn * 32 + 8 * g + 4 * h);
     }
   }
-  // E = L: from the L operand's k-tile kt in LDS (base sL, rows of the tile
-  // at kRowBytes each), if kt holds some of this thread's columns.  kb is
-  // the first k-tile of the tile's column block (col0 / 64 for 16-bit T).
+  // Before capture: columns in k-tiles past the contraction are never
+  // captured and stay zero (they are the zero padding of E).
   __device__ __forceinline__ void zero() {
     if constexpr (kEnabled) {
 #pragma unroll
@@ -730,9 +729,12 @@ struct EPrefetch {
           for (int g = 0; g < 4; ++g) v[fm][fn][g] = uint2{0u, 0u};
     }
   }
-  // Row il = wr + 32 fm + lr sits at fa.row0L + 32 fm kRowBytes with the
-  // chunk swizzle fa.swL0 / fa.swL1 (even / odd fm), as for the fragment
-  // reads.
+  // E = L: this thread's values from the L operand's k-tile kt in LDS (base
+  // sL, rows of the tile at kRowBytes each), if kt holds some of its
+  // columns; kb is the first k-tile of the tile's column block (col0 / 64
+  // for 16-bit T).  Row il = wr + 32 fm + lr sits at fa.row0L + 32 fm
+  // kRowBytes with the chunk swizzle fa.swL0 / fa.swL1 (even / odd fm), as
+  // for the fragment reads.
   __device__ __forceinline__ void capture(int kt, const char* sL, int kb, const FragAddr& fa) {
     if constexpr (kEnabled) {
       const int d = kt - kb;
