@@ -690,33 +690,16 @@ __device__ __forceinline__ void acc_zero(Acc<T, TM, TN>& acc) {
 // for il = wr + 32 fm + lr, jl = wc + 32 fn + 8 g + 4 h.  Tiles up to 192
 // have the registers to hold it (8 bytes per (fm, fn, g)) through the main
 // loop, so it never sits between the last MFMA and the stores; the 256 tile
-// loads it in the epilogue.  The update loads it from global memory before
-// the main loop (load); the symmetric products, where E is the L operand,
-// take it from L's k-tiles col0 / 64 .. (col0 + TN) / 64 while they are in
-// LDS (capture), so it costs no HBM reads and does not hold up the first
-// k-tile.
+// loads it in the epilogue.  E is always one of the operands in LDS: the
+// symmetric products take it from L's k-tiles col0 / 64 .. (col0 + TN) / 64
+// (capture), the update, where E = X and R = X^T, from R's k-tiles row0 / 64
+// .. (row0 + TM) / 64, transposed (capture_t).  So it costs no HBM reads and
+// does not hold up the first k-tile.
 template <typename T, int TM, int TN>
 struct EPrefetch {
   static constexpr int FM = TM / 64, FN = TN / 64;
   static constexpr bool kEnabled = FM * FN <= 9 && sizeof(T) == 2;
-  static constexpr int kLoads = kEnabled ? FM * FN * 4 : 0;  // vector loads per thread
   uint2 v[kEnabled ? FM : 1][kEnabled ? FN : 1][4];
-  __device__ __forceinline__ void load(const T* E, int64_t ld, int64_t row0, int64_t col0) {
-    if constexpr (kEnabled) {
-      if (!E) return;
-      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-      const int lr = lane & 31, h = lane >> 5;
-      const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * (TN / 2);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            v[fm][fn][g] = *reinterpret_cast<const uint2*>(E + (row0 + wr + fm * 32 + lr) * ld + col0 + wc +
-                                                           fn * 32 + 8 * g + 4 * h);
-    }
-  }
   // Before capture: columns in k-tiles past the contraction are never
   // captured and stay zero (they are the zero padding of E).
   __device__ __forceinline__ void zero() {
@@ -755,6 +738,47 @@ struct EPrefetch {
                                                            8 * h);
           }
         }
+    }
+  }
+  // E = R^T (the update: E = X, R = X^T): this thread's values from the R
+  // operand's k-tile kt in LDS (base sR, rows of the tile's R panel at
+  // kRowBytes each), if kt holds some of its rows; kb is the first k-tile
+  // of the tile's row block (row0 / 64).  E[il][jl + e] = R[jl + e][il]:
+  // one 2-byte read per element, from R rows jl .. jl + 3 at k-column
+  // il - 64 (kt - kb).  A 32-row group of il lies in one k-tile, so the
+  // test is uniform per wave.  Row r = wc + 32 fn + 8 g + 4 h + e has
+  // swz(r) = (4 h + e) ^ ((wc / 8 + 4 fn + g) & 7) with wc / 8 = 0 or 4
+  // (mod 8), so a chunk index xor swz(r) is a per-thread part xor the
+  // constant e ^ ((4 fn + g) & 7): eight address registers, recomputed from
+  // d at each capture rather than held through the main loop.
+  __device__ __forceinline__ void capture_t(int kt, const char* sR, int kb) {
+    if constexpr (kEnabled) {
+      static_assert(TN % 64 == 0, "wc / 8 must be 0 or 4 mod 8");
+      const int d = kt - kb;
+      if (d < 0 || d >= TM / 64) return;
+      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+      const int lr = lane & 31, h = lane >> 5;
+      const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * (TN / 2);
+      const char* rb = sR + (wc + 4 * h) * kRowBytes + (lr & 7) * 2;
+      const int sx = (4 * h) ^ ((wc >> 3) & 7);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int i0 = wr + fm * 32 - 64 * d;  // k-column of lane group's row il = wr + 32 fm (uniform)
+        if (i0 < 0 || i0 >= 64) continue;
+        const int cx = ((i0 + lr) >> 3) ^ sx;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint32_t q[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int k = e ^ ((4 * fn + g) & 7);
+              q[e] = *reinterpret_cast<const uint16_t*>(rb + (32 * fn + 8 * g + e) * kRowBytes + ((cx ^ k) << 4));
+            }
+            v[fm][fn][g] = uint2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+          }
+      }
     }
   }
   // E[il][jl..jl+3] as floats: from the registers, or loaded now.
@@ -972,12 +996,19 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   OutT* Y = p.Y + bz * p.sY;
   T* YT = p.YT ? p.YT + bz * p.sYT : nullptr;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
+  // E is X and the R operand X^T, so E's tile is the transpose of the R
+  // panel's k-tiles row0 / BK .. (row0 + TM) / BK, taken from LDS as they
+  // pass (rows past the contraction are X's zero padding).
   using EP = EPrefetch<T, TM, TN>;
   EP ep;
+  ep.zero();
   A acc;
   acc_zero(acc);
-  mainloop<T, TM, TN, EP::kLoads, G>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
-                                  [&] { ep.load(E, p.lde, row0, col0); }, [](int, const char*, const FragAddr&) {});
+  const int kb = (int)(row0 / BK);
+  mainloop<T, TM, TN, 0, G>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, false, [] {},
+                            [&](int kt, const char* sL, const FragAddr&) {
+                              if (E) ep.capture_t(kt, sL + TM * kRowBytes, kb);
+                            });
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
