@@ -293,21 +293,32 @@ hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents e
   return launch_kernel(k_sym<T, TILE, GRAM_INPUT>, tiles_grid, dim3(kThreads), s, ev, a);
 }
 
-template <typename T, typename OutT, int TILE>
-hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+template <typename T, typename OutT, int TILE, bool CAP>
+hipError_t launch_nt_cap(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
   constexpr int TN = nn_tile_n(TILE);
   const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
   const dim3 flat((unsigned)(per * batch));
   a.batch = (int)batch;
   if constexpr (kHasPairKernels<T, TILE>) {
     if (use_pair(TILE, (int)sizeof(T), per * batch))
-      return launch_kernel(k_nt<T, OutT, TILE, TN, 2>, flat, dim3(kThreads), s, ev, a);
+      return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP>, flat, dim3(kThreads), s, ev, a);
   }
   if constexpr (TILE <= 192) {
     if (use_persistent(TILE, per * batch, a.K / (kRowBytes / (int)sizeof(T))))
-      return launch_kernel(k_nt_loop<T, OutT, TILE, TN>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
+      return launch_kernel(k_nt_loop<T, OutT, TILE, TN, 1, CAP>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
   }
-  return launch_kernel(k_nt<T, OutT, TILE, TN>, flat, dim3(kThreads), s, ev, a);
+  return launch_kernel(k_nt<T, OutT, TILE, TN, 1, CAP>, flat, dim3(kThreads), s, ev, a);
+}
+
+// Updates with an E term (the standard form) take the kernels that capture
+// E from LDS, where the tile has the registers for it; E-free updates (the
+// Gram form) and the other tiles take the kernels without the capture.
+template <typename T, typename OutT, int TILE>
+hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+  if constexpr (EPrefetch<T, TILE, nn_tile_n(TILE)>::kEnabled) {
+    if (a.E) return launch_nt_cap<T, OutT, TILE, true>(a, batch, s, ev);
+  }
+  return launch_nt_cap<T, OutT, TILE, false>(a, batch, s, ev);
 }
 
 // One Newton-Schulz run over a batch, for internal type T and I/O type IO.

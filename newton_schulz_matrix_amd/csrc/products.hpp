@@ -694,12 +694,30 @@ __device__ __forceinline__ void acc_zero(Acc<T, TM, TN>& acc) {
 // symmetric products take it from L's k-tiles col0 / 64 .. (col0 + TN) / 64
 // (capture), the update, where E = X and R = X^T, from R's k-tiles row0 / 64
 // .. (row0 + TM) / 64, transposed (capture_t).  So it costs no HBM reads and
-// does not hold up the first k-tile.
+// does not hold up the first k-tile.  The update kernels built without the
+// capture load E from global memory before the main loop instead (load).
 template <typename T, int TM, int TN>
 struct EPrefetch {
   static constexpr int FM = TM / 64, FN = TN / 64;
   static constexpr bool kEnabled = FM * FN <= 9 && sizeof(T) == 2;
+  static constexpr int kLoads = kEnabled ? FM * FN * 4 : 0;  // vector loads per thread
   uint2 v[kEnabled ? FM : 1][kEnabled ? FN : 1][4];
+  __device__ __forceinline__ void load(const T* E, int64_t ld, int64_t row0, int64_t col0) {
+    if constexpr (kEnabled) {
+      if (!E) return;
+      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+      const int lr = lane & 31, h = lane >> 5;
+      const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * (TN / 2);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            v[fm][fn][g] = *reinterpret_cast<const uint2*>(E + (row0 + wr + fm * 32 + lr) * ld + col0 + wc +
+                                                           fn * 32 + 8 * g + 4 * h);
+    }
+  }
   // Before capture: columns in k-tiles past the contraction are never
   // captured and stay zero (they are the zero padding of E).
   __device__ __forceinline__ void zero() {
@@ -982,7 +1000,9 @@ __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
 }
 
 // Y = alpha E + gamma B (X^T)^T on TM x TN tiles: the update of both forms.
-template <typename T, typename OutT, int TM, int TN, int G>
+// CAP: E is taken from the X^T panel in LDS during the main loop; otherwise
+// it is loaded from global memory before the main loop (or absent).
+template <typename T, typename OutT, int TM, int TN, int G, bool CAP>
 __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn, int bz) {
   using A = Acc<T, TM, TN>;
   constexpr int FM = A::FM, FN = A::FN;
@@ -996,19 +1016,32 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   OutT* Y = p.Y + bz * p.sY;
   T* YT = p.YT ? p.YT + bz * p.sYT : nullptr;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  // E is X and the R operand X^T, so E's tile is the transpose of the R
-  // panel's k-tiles row0 / BK .. (row0 + TM) / BK, taken from LDS as they
-  // pass (rows past the contraction are X's zero padding).
   using EP = EPrefetch<T, TM, TN>;
   EP ep;
-  ep.zero();
   A acc;
   acc_zero(acc);
-  const int kb = (int)(row0 / BK);
-  mainloop<T, TM, TN, 0, G>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, false, [] {},
-                            [&](int kt, const char* sL, const FragAddr&) {
-                              if (E) ep.capture_t(kt, sL + TM * kRowBytes, kb);
-                            });
+  if constexpr (CAP) {
+    // E is X and the R operand X^T, so E's tile is the transpose of the R
+    // panel's k-tiles row0 / BK .. (row0 + TM) / BK, taken from LDS as they
+    // pass (rows past the contraction are X's zero padding).
+    ep.zero();
+    const int kb = (int)(row0 / BK);
+    mainloop<T, TM, TN, 0, G>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, false, [] {},
+                              [&](int kt, const char* sL, const FragAddr&) {
+                                if constexpr (EP::kEnabled) {
+                                  // E is set whenever CAP is; without the test the
+                                  // 192 tile's schedule spills registers.
+                                  if (E) ep.capture_t(kt, sL + TM * kRowBytes, kb);
+                                }
+                              });
+  } else {
+    // E-free updates (the Gram form) take this path.  Its schedule is the
+    // one measured fastest for them; built without these E registers the
+    // 192 tile ran 40 % slower.
+    mainloop<T, TM, TN, EP::kLoads, G>(Lg, ldb_bytes, Rg, ldxt_bytes, 0, p.K / BK, acc, EP::kLoads > 0 && E,
+                                       [&] { ep.load(E, p.lde, row0, col0); },
+                                       [](int, const char*, const FragAddr&) {});
+  }
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 31, h = lane >> 5;
@@ -1129,17 +1162,17 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
 // One work-group per tile on a one-dimensional grid over the tiles of all
 // matrices: the list (matrix by matrix, each in grouped_tile order) is cut
 // into one contiguous piece per XCD.
-template <typename T, typename OutT, int TM, int TN, int G = 1>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int pos = xcd_order(blockIdx.x, per * p.batch);
   int tm, tn;
   grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-  nt_tile<T, OutT, TM, TN, G>(p, tm, tn, pos / per);
+  nt_tile<T, OutT, TM, TN, G, CAP>(p, tm, tn, pos / per);
 }
 
 // Persistent form of k_nt (see k_sym_loop).
-template <typename T, typename OutT, int TM, int TN, int G = 1>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int total = per * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
@@ -1147,7 +1180,7 @@ __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
     const int pos = base + piece, bz = pos / per;
     int tm, tn;
     grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-    nt_tile<T, OutT, TM, TN, G>(p, tm, tn, bz);
+    nt_tile<T, OutT, TM, TN, G, CAP>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }
