@@ -22,14 +22,17 @@ Prints one JSON line.  Besides the driver's fields it carries:
                          step and its fraction of the fp16/bf16 dense peak;
   standard_form          the same measurement for the standard form;
   roofline               the dominant kernel's achieved rate (HIP events
-                         bound to each of its launches, in an instrumented
-                         run of the same number of steps right after the
-                         timed region);
-  kernels                per-kernel-kind average times (warm-up calls);
+                         bound to each launch, in an instrumented run of the
+                         same number of steps right after the timed region);
+  kernels                per-kernel-kind average launch times (the
+                         instrumented run);
   ms_per_step_instrumented, ms_p10_p50_p90
                          the instrumented run's time per call and its
                          per-call spread.
-  cpu_baseline           the fp64 oracle on the host cores (bounded sample).
+  cpu_baseline           the fp64 oracle on the host cores (bounded sample),
+                         with the host CPU model;
+  quality                (ROOT workload) the MSE of the result against the
+                         exact polar factor of the split's robust part.
 """
 
 from __future__ import annotations
@@ -73,7 +76,7 @@ def parse():
                     help="one ROWS x COLS column-scaled bf16 matrix instead "
                          "of --workload")
     ap.add_argument("--mode", default="gram", choices=["gram", "standard"])
-    ap.add_argument("--internal", default=None, choices=[None, "fp16", "bf16"])
+    ap.add_argument("--internal", default=None, choices=[None, "fp16"])
     ap.add_argument("--restart-mask", type=int, default=1 << 4)
     ap.add_argument("--tile", type=int, default=0, choices=[0, 128, 192, 256],
                     help="force the products' tile edge (0: automatic)")
@@ -245,32 +248,23 @@ def make_step(inputs, mode, args, kind):
     return step
 
 
-def run_form(inputs, mode, steps, warmup, args, kind="ns", trace_kinds=None):
+def run_form(inputs, mode, steps, warmup, args, kind="ns"):
     """Warm up, time `steps` plain steps, then `steps` instrumented ones.
 
     The timed region (`ms_per_step`) runs the calls exactly as a user would,
     with one event at each end.  Timing single launches needs HIP events on
     the stream, which leave the GPU idle for several microseconds around
-    each traced launch, so the per-launch times (the roofline and kernel
-    figures) and the per-call spread come from a second run of `steps`
-    calls, instrumented, right after the timed region.
+    each traced launch, so the per-launch times (the roofline and the
+    per-kernel figures) and the per-call spread come from a second run of
+    `steps` calls with every launch traced, right after the timed region.
     """
     import torch
     step = make_step(inputs, mode, args, kind)
-    # One untraced step first: the first launch of each kernel also loads
-    # its code object.  Then warm-up steps with every kind traced, to find
-    # the dominant kernel.
-    step()
-    torch.cuda.synchronize()
-    per_call = 64 * len(inputs)
-    ev = Events(2 * per_call * max(warmup, 1))
-    tr = make_trace(ev, per_call * max(warmup, 1), 0xFFFFFFFF)
+    # Untraced warm-up; the first launch of each kernel also loads its code
+    # object.
     for _ in range(max(warmup, 1)):
-        step(tr)
+        step()
     torch.cuda.synchronize()
-    warm = trace_stats(ev, tr)
-    ev.close()
-    dominant = max(warm, key=lambda k: warm[k]["ms"])
 
     # Timed region: `steps` plain calls.
     start = torch.cuda.Event(enable_timing=True)
@@ -285,15 +279,11 @@ def run_form(inputs, mode, steps, warmup, args, kind="ns", trace_kinds=None):
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
 
-    # Instrumented run: events around every launch of the traced kinds and
-    # at every call boundary.
-    mask = 0
-    kinds = trace_kinds if trace_kinds is not None else [dominant]
-    from newton_schulz_matrix_amd._binding import KERNEL_KINDS
-    for k in kinds:
-        mask |= 1 << KERNEL_KINDS.index(k)
+    # Instrumented run: events bound to every launch and at every call
+    # boundary.
+    per_call = 64 * len(inputs)
     ev = Events(2 * per_call * steps)
-    tr = make_trace(ev, per_call * steps, mask)
+    tr = make_trace(ev, per_call * steps, 0xFFFFFFFF)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     marks[0].record()
@@ -309,10 +299,11 @@ def run_form(inputs, mode, steps, warmup, args, kind="ns", trace_kinds=None):
 
     timed = trace_stats(ev, tr)
     ev.close()
+    dominant = max(timed, key=lambda k: timed[k]["ms"])
     return {"ms_per_step": total_ms / steps, "wall_s": wall,
             "ms_per_step_instrumented": inst_ms / steps,
             "ms_p10": pct(0.1), "ms_p50": pct(0.5), "ms_p90": pct(0.9),
-            "dominant": dominant, "warm_kernels": warm, "timed_kernels": timed}
+            "dominant": dominant, "timed_kernels": timed}
 
 
 def _code_only(text):
@@ -394,10 +385,51 @@ def cpu_baseline(m_cpu, mode, restart_mask):
                if d.get("user_api") == "blas"]
     cores = int(max(threads)) if threads else len(os.sched_getaffinity(0))
     return {"value": 1.0 / dt, "unit": "orth/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "cpus_allowed": len(os.sched_getaffinity(0)),
             "sample": f"full {m64.shape[0]}x{m64.shape[1]} {mode}-form "
                       f"orthogonalizations in fp64 (numpy/OpenBLAS): median "
                       f"of 3 after 1 warm-up, {dt:.1f} s each"}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def root_quality(host_input, mode, args):
+    """The ROOT workload's reported quantity: the orthogonalization MSE of
+    NS(B) against B's exact polar factor, ||NS(B) - polar(B)||_F^2 / n
+    (B the robust part of the split, n its smaller side), with the polar
+    factor from LAPACK's symmetric eigensolver on the host."""
+    import numpy as np
+    import torch
+    import newton_schulz_matrix_amd as nsa
+    m = host_input.to("cuda:0")
+    b, _ = nsa.soft_threshold_split(m)
+    x = b.clone()
+    nsa.orthogonalize(x, mode=mode, restart_mask=args.restart_mask)
+    torch.cuda.synchronize()
+    b64 = b.double().cpu().numpy()
+    out = x.double().cpu().numpy()
+    wide = b64.shape[0] <= b64.shape[1]
+    bw = b64 if wide else b64.T
+    w, v = np.linalg.eigh(bw @ bw.T)
+    polar = (v / np.sqrt(w)) @ v.T @ bw
+    if not wide:
+        polar = polar.T
+    mse = float(np.sum((out - polar) ** 2) / min(b64.shape))
+    return {"mse_vs_polar": mse, "form": mode,
+            "definition": "||NS(B) - polar(B)||_F^2 / min(rows, cols); "
+                          "polar from numpy.linalg.eigh of B B^T"}
 
 
 def copy_calibration(args):
@@ -463,7 +495,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
 
     dom = res["dominant"]
-    ks = res["timed_kernels"].get(dom) or res["warm_kernels"][dom]
+    ks = res["timed_kernels"][dom]
     avg_ms = ks["ms"] / ks["launches"]
     if dom in ("norm", "stage", "threshold"):
         achieved = ks["bytes"] / ks["launches"] / (avg_ms * 1e-3) / 1e9
@@ -484,9 +516,9 @@ def main():
     roof["launches_timed"] = ks["launches"]
 
     kernels = {}
-    for k, s in res["warm_kernels"].items():
+    for k, s in res["timed_kernels"].items():
         avg = s["ms"] / s["launches"]
-        entry = {"launches_per_step": s["launches"] / max(args.warmup, 1),
+        entry = {"launches_per_step": s["launches"] / args.steps,
                  "avg_ms": avg}
         if s["flops"] > 0:
             entry["tflops"] = s["flops"] / s["launches"] / (avg * 1e-3) / 1e12
@@ -533,6 +565,8 @@ def main():
             "tflops": total_flops("standard") / (std["ms_per_step"] * 1e-3)
             / 1e12,
             "gram_speedup": std["ms_per_step"] / ms}
+    if kind == "root":
+        out["quality"] = root_quality(host_inputs[0], args.mode, args)
     if not args.no_cpu_baseline:
         first = host_inputs[0]
         sample = first if first.dim() == 2 else first[0]

@@ -27,8 +27,8 @@
  * Error behaviour.  Arguments are checked on the host before anything is
  * enqueued; a bad argument returns an error code and enqueues nothing.
  * A HIP launch failure returns NS_ERR_HIP (the stream may then hold part of
- * the work).  Non-finite results are reported asynchronously through the
- * optional device status word (ns_options.d_status).
+ * the work).  Non-finite values are reported asynchronously through the
+ * optional device status word (see "Status word" below).
  */
 #ifndef NSORTHO_H
 #define NSORTHO_H
@@ -48,8 +48,32 @@ typedef enum {
   NS_ERR_INVALID_ARG = 1,       /* a size, pointer, step count or option is out of range */
   NS_ERR_UNSUPPORTED_DTYPE = 2, /* dtype or internal dtype combination not supported */
   NS_ERR_WORKSPACE = 3,         /* workspace missing, misaligned or smaller than required */
-  NS_ERR_HIP = 4                /* a HIP runtime call or kernel launch failed */
+  NS_ERR_HIP = 4,               /* a HIP runtime call or kernel launch failed */
+  NS_ERR_NONFINITE = 5          /* a NaN or Inf was produced on the device; reported only
+                                   through the device status word, never returned */
 } ns_status;
+
+/*
+ * Status word.  An optional device int32 owned by the caller, who clears it
+ * before the call; kernels only OR bits into it, so one word may collect
+ * several calls.  When any kernel of the call produces a NaN or Inf (or,
+ * for stored 16-bit values, a value that rounds to Inf) it ORs in
+ * NS_ERR_NONFINITE together with one NS_STATUS_AT_* bit naming where:
+ * NS_STATUS_CODE(word) is then NS_ERR_NONFINITE, and NS_OK while the word
+ * is clear of it.  The Gram-NS article ("Stability challenges and
+ * solutions") names this failure: in half precision the Gram matrix of the
+ * naive iteration can develop negative eigenvalues and the iteration
+ * diverges to Inf.  NS_STATUS_GUARD_RESTART reports an on-demand restart of
+ * the guarded Gram iteration (ns_options.guard); it is not an error.
+ */
+#define NS_STATUS_CODE(word) ((ns_status)((word) & 0xff))
+#define NS_STATUS_AT_INPUT (1 << 8)    /* the input's Frobenius norm is not finite */
+#define NS_STATUS_AT_STATE (1 << 9)    /* an n x n intermediate: A, b A + c A^2 (standard form);
+                                          R, Z', Q, V (Gram form) */
+#define NS_STATUS_AT_ITERATE (1 << 10) /* an intermediate X (between steps, or at a restart) */
+#define NS_STATUS_AT_OUTPUT (1 << 11)  /* the result written to the caller's matrix */
+#define NS_STATUS_AT_SPLIT (1 << 12)   /* soft-threshold split: lambda, B or O */
+#define NS_STATUS_GUARD_RESTART (1 << 16)
 
 typedef enum { NS_BF16 = 0, NS_FP16 = 1, NS_FP32 = 2 } ns_dtype;
 
@@ -99,12 +123,15 @@ typedef struct ns_options {
   /* Added to ||X||_F before dividing.  Default 1e-7.  A zero matrix gives a
    * zero result. */
   float eps;
-  /* Operand type of the matrix products: -1 = automatic (NS_FP16 for bf16
-   * and fp16 input, NS_FP32 for fp32 input), NS_FP16 or NS_BF16 for 16-bit
-   * input, NS_FP32 for fp32 input.  Products always accumulate in fp32. */
+  /* Operand type of the matrix products: -1 = automatic, NS_FP16 for bf16
+   * and fp16 input, NS_FP32 for fp32 input; any other value (NS_BF16
+   * included) gives NS_ERR_UNSUPPORTED_DTYPE.  Products always accumulate in
+   * fp32.  bf16 operands are not offered: with 8 mantissa bits in every
+   * stored intermediate the iteration misses the 1e-2 relative error bar
+   * for 16-bit input (the Gram-NS article keeps float16 in the key steps). */
   int32_t internal;
-  /* Optional device int32.  When not NULL, kernels set it to 1 if any output
-   * element is NaN or Inf.  The caller clears it; it is never cleared here. */
+  /* Optional device status word (see "Status word").  Kernels check their
+   * results for NaN and Inf only when it is set. */
   int32_t* d_status;
   /* Optional launch trace (see ns_trace); NULL for none. */
   ns_trace* trace;
@@ -143,9 +170,16 @@ size_t ns_workspace_size(int64_t rows, int64_t cols, int64_t batch,
  *            caller; its contents on entry do not matter.
  *   stream   the HIP stream all work is enqueued on.
  *
- * Gram form with 16-bit internal operands: the product of |a_k| over any run
- * of steps without a restart must stay below 2^15 (the accumulated Q is held
- * in 16 bits); otherwise NS_ERR_INVALID_ARG.
+ * Coefficient range: every stored intermediate must stay below half of its
+ * storage type's largest value in exact arithmetic, or the call returns
+ * NS_ERR_INVALID_ARG.  The check follows one singular value s in [0, 1]
+ * of the scaled input through the steps (every matrix of both forms is a
+ * function of the singular values, and its entries are bounded by its
+ * spectral norm): X (held as 2^10 X in fp16), A = s^2 and b A + c A^2
+ * (standard form); R, Z' = b R + c R^2, Q, V = R Z and X at a restart
+ * (Gram form); and the result in the caller's dtype.  The 16-bit limit is
+ * 2^15.  For the Gram form the accumulated Q reaches the product of the
+ * a_k between restarts, so a naive run of nine tuned steps is refused.
  */
 ns_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld,
                            ns_dtype dtype, int32_t steps, const float* a,
@@ -184,7 +218,12 @@ ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows,
  *   lambda   >= 0: use it.  < 0: lambda = mult * median|M|, with the median
  *            the ceil(numel/2)-th smallest |M| (1-based), found exactly
  *            on the device by a radix select over the bit patterns.
- *   d_lambda_out  optional device float receiving lambda (fp32).
+ *   d_lambda_out  optional device float receiving lambda.  lambda is
+ *            formed in fp32: mult * median rounded once to fp32 (the
+ *            median of 16-bit or fp32 input is exact in fp32), and every
+ *            clip decision compares |M| with that fp32 value.
+ *   d_status optional device status word (see "Status word"): a NaN or Inf
+ *            in lambda, B or O ORs in NS_ERR_NONFINITE | NS_STATUS_AT_SPLIT.
  *   workspace   device memory of ns_soft_threshold_workspace_size(...)
  *            bytes, 256-byte aligned.
  * B is rounded to `dtype` (clipped entries become lambda rounded to nearest
@@ -197,8 +236,8 @@ size_t ns_soft_threshold_workspace_size(int64_t numel, ns_dtype dtype);
 ns_status ns_soft_threshold_split(const void* M, void* B, void* O,
                                   int64_t numel, ns_dtype dtype, float lambda,
                                   float mult, float* d_lambda_out,
-                                  void* workspace, size_t workspace_bytes,
-                                  ns_stream_t stream);
+                                  int32_t* d_status, void* workspace,
+                                  size_t workspace_bytes, ns_stream_t stream);
 
 /*
  * One Muon optimizer step on `batch` equal-shape weight matrices (batch = 1
@@ -239,6 +278,24 @@ ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch,
                        const float* a, const float* b, const float* c,
                        ns_mode mode, const ns_options* opt, void* workspace,
                        size_t workspace_bytes, ns_stream_t stream);
+
+/*
+ * The kernel builds one call would launch, for inspection (host only;
+ * touches no device).  Arguments as for ns_workspace_size, plus the step
+ * count.  Writes a NUL-terminated, space-separated list of the distinct
+ * builds in launch order into buf (truncated to len bytes; buf may be NULL)
+ * and returns the length the whole list needs including the NUL, or -1 for
+ * invalid arguments.  Entries: sumsq<io>, stage<io,op>; xxt<op,tile,form>
+ * (X X^T) and nn<op,tile,form> (n x n products); upd<op,op,tile,form,e>
+ * (intermediate X updates) and out<op,io,tile,form,e> (the final product);
+ * op is the product operand type, form one of tile (a work-group per tile),
+ * loop (a persistent grid), pair and pairloop (the same, built for two
+ * work-groups per compute unit), e is E when the a X term is taken from
+ * LDS, Eg when it is read from global memory and noE when there is none.
+ */
+int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch,
+                        ns_dtype dtype, ns_mode mode, int32_t steps,
+                        const ns_options* opt, char* buf, size_t len);
 
 /* Static description of a status code. */
 const char* ns_status_string(ns_status s);

@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence, Tuple, Union
+from typing import List, Optional, Sequence, Tuple, Union
 
 import torch
 
@@ -21,6 +21,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libnsortho.so")
 
 NS_OK = 0
+NS_ERR_NONFINITE = 5
+# Status word bits (the device int32 passed as `status`).
+STATUS_AT_INPUT = 1 << 8
+STATUS_AT_STATE = 1 << 9
+STATUS_AT_ITERATE = 1 << 10
+STATUS_AT_OUTPUT = 1 << 11
+STATUS_AT_SPLIT = 1 << 12
+STATUS_GUARD_RESTART = 1 << 16
 NS_BF16, NS_FP16, NS_FP32 = 0, 1, 2
 NS_STANDARD, NS_GRAM = 0, 1
 NS_MAX_STEPS = 16
@@ -99,7 +107,13 @@ _SIGNATURES = {
                                  ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                  ctypes.c_void_p, ctypes.c_void_p,
-                                 ctypes.c_size_t, ctypes.c_void_p]),
+                                 ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]),
+    "ns_plan_kernels": (ctypes.c_int64,
+                        [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                         ctypes.c_int, ctypes.c_int, ctypes.c_int32,
+                         ctypes.POINTER(Options), ctypes.c_char_p,
+                         ctypes.c_size_t]),
     "ns_muon_workspace_size": (ctypes.c_size_t,
                                [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                 ctypes.c_int, ctypes.c_int,
@@ -199,11 +213,20 @@ def _stream_handle(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def status_code(word: int) -> int:
+    """The ns_status held in a status word's low byte (NS_STATUS_CODE)."""
+    return int(word) & 0xFF
+
+
 def _workspace(nbytes: int, device: torch.device,
                workspace: Optional[torch.Tensor]) -> Tuple[int, int, torch.Tensor]:
     """A 256-byte aligned device buffer of at least nbytes (from torch)."""
     if workspace is None:
         workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    elif not workspace.is_cuda or workspace.device != device:
+        raise ValueError(f"workspace must be a device tensor on {device}")
+    elif not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     ptr = workspace.data_ptr()
     pad = (-ptr) % 256
     avail = workspace.numel() * workspace.element_size() - pad
@@ -217,6 +240,24 @@ def workspace_size(rows: int, cols: int, batch: int = 1,
     opt = make_options(restart_mask, 1e-7, internal, tile=tile)
     return int(lib().ns_workspace_size(rows, cols, batch, dtype_code(dtype),
                                        _MODE_CODE[mode], ctypes.byref(opt)))
+
+
+def plan_kernels(rows: int, cols: int, batch: int = 1,
+                 dtype: torch.dtype = torch.bfloat16, mode: str = "standard",
+                 steps: int = 5, restart_mask: int = 1 << 4,
+                 internal: Optional[str] = None, tile: int = 0) -> List[str]:
+    """The kernel builds one call would launch (host only, no device)."""
+    opt = make_options(restart_mask, 1e-7, internal, tile=tile)
+    need = int(lib().ns_plan_kernels(rows, cols, batch, dtype_code(dtype),
+                                     _MODE_CODE[mode], steps,
+                                     ctypes.byref(opt), None, 0))
+    if need < 0:
+        raise NSError(1, "ns_plan_kernels")
+    buf = ctypes.create_string_buffer(need)
+    lib().ns_plan_kernels(rows, cols, batch, dtype_code(dtype),
+                          _MODE_CODE[mode], steps, ctypes.byref(opt), buf,
+                          need)
+    return buf.value.decode().split()
 
 
 def _check_matrix(x: torch.Tensor, ndim: int) -> None:
@@ -346,15 +387,24 @@ def muon_workspace_size(rows: int, cols: int, batch: int = 1,
 def soft_threshold_split(m: torch.Tensor, lam: Optional[float] = None,
                          mult: float = 3.0, outliers: bool = True,
                          out_b: Optional[torch.Tensor] = None,
-                         lambda_out: Optional[torch.Tensor] = None):
+                         lambda_out: Optional[torch.Tensor] = None,
+                         status: Optional[torch.Tensor] = None):
     """ROOT split of a contiguous device tensor: returns (B, O or None).
 
-    ``lambda_out`` (device fp32, one element) receives the threshold.
+    ``lambda_out`` (device fp32, one element) receives the threshold;
+    ``status`` (device int32) is the status word.  ``out_b`` (optional)
+    receives B: a contiguous tensor with m's dtype, device and number of
+    elements (it may be m itself).
     """
     if not m.is_cuda or not m.is_contiguous():
         raise ValueError("expects a contiguous device tensor")
     code = dtype_code(m.dtype)
     numel = m.numel()
+    if out_b is not None:
+        if out_b.dtype != m.dtype or out_b.device != m.device:
+            raise ValueError("out_b must have m's dtype and device")
+        if out_b.numel() != numel or not out_b.is_contiguous():
+            raise ValueError("out_b must be contiguous with m's number of elements")
     b = torch.empty_like(m) if out_b is None else out_b
     o = torch.empty_like(m) if outliers else None
     need = int(lib().ns_soft_threshold_workspace_size(numel, code))
@@ -367,10 +417,15 @@ def soft_threshold_split(m: torch.Tensor, lam: Optional[float] = None,
         if lambda_out.dtype != torch.float32 or not lambda_out.is_cuda:
             raise TypeError("lambda_out must be a device fp32 tensor")
         lptr = lambda_out.data_ptr()
+    sptr = None
+    if status is not None:
+        if status.dtype != torch.int32 or not status.is_cuda:
+            raise TypeError("status must be a device int32 tensor")
+        sptr = status.data_ptr()
     st = lib().ns_soft_threshold_split(
         ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(b.data_ptr()),
         ctypes.c_void_p(o.data_ptr() if o is not None else None), numel, code,
-        lam_arg, float(mult), ctypes.c_void_p(lptr), ctypes.c_void_p(wptr),
-        wbytes, _stream_handle(m.device))
+        lam_arg, float(mult), ctypes.c_void_p(lptr), ctypes.c_void_p(sptr),
+        ctypes.c_void_p(wptr), wbytes, _stream_handle(m.device))
     _check(st, "ns_soft_threshold_split")
     return b, o

@@ -6,6 +6,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <string>
+#include <vector>
 #include <stdint.h>
 #include <string.h>
 
@@ -48,6 +50,11 @@ struct Plan {
 // (192 x 256 update tiles were measured slower than 192 x 192 at 4096 x 14336).
 constexpr int nn_tile_n(int edge) { return edge; }
 
+// Products run on fp16 operands for 16-bit input and on fp32 operands for
+// fp32 input.  bf16 operands are refused: with 8 mantissa bits in every
+// stored intermediate the iteration misses the 1e-2 relative error bar of
+// 16-bit input on ordinary shapes (the Gram-NS article's stabilized
+// iteration keeps float16 in its key steps for this reason).
 bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
   const int req = opt ? opt->internal : -1;
   if (io == NS_FP32) {
@@ -58,10 +65,6 @@ bool resolve_internal(ns_dtype io, const ns_options* opt, ns_dtype* out) {
   if (io != NS_BF16 && io != NS_FP16) return false;
   if (req == -1 || req == NS_FP16) {
     *out = NS_FP16;
-    return true;
-  }
-  if (req == NS_BF16) {
-    *out = NS_BF16;
     return true;
   }
   return false;
@@ -273,24 +276,45 @@ bool use_pair(int edge, int esz, int64_t tiles) {
   return edge == 128 && esz == 2 && tiles >= 2 * (int64_t)kPersistentGroups;
 }
 
+// The kernel build a product launch takes: one work-group per tile or a
+// persistent grid, for one or two work-groups per compute unit.
+enum class Form { kTile, kLoop, kPairTile, kPairLoop };
+
+Form sym_form(int edge, int esz, int64_t tiles, int64_t ktiles) {
+  if (use_pair(edge, esz, tiles)) return use_persistent(edge, tiles, ktiles) ? Form::kPairLoop : Form::kPairTile;
+  if (edge <= 192 && use_persistent(edge, tiles, ktiles)) return Form::kLoop;
+  return Form::kTile;
+}
+
+Form nt_form(int edge, int esz, int64_t tiles, int64_t ktiles) {
+  if (use_pair(edge, esz, tiles)) return Form::kPairTile;
+  if (edge <= 192 && use_persistent(edge, tiles, ktiles)) return Form::kLoop;
+  return Form::kTile;
+}
+
 template <typename T, int TILE, bool GRAM_INPUT>
 hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
   const int64_t ntri = (int64_t)a.tiles * (a.tiles + 1) / 2;
   const int ktiles = a.K / (kRowBytes / (int)sizeof(T));
   const dim3 tiles_grid((unsigned)ntri, (unsigned)batch);
   a.batch = (int)batch;
-  if constexpr (kHasPairKernels<T, TILE>) {
-    if (use_pair(TILE, (int)sizeof(T), ntri * batch)) {
-      if (use_persistent(TILE, ntri * batch, ktiles))
+  switch (sym_form(TILE, (int)sizeof(T), ntri * batch, ktiles)) {
+    case Form::kPairLoop:
+      if constexpr (kHasPairKernels<T, TILE>)
         return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2>, dim3(2 * kPersistentGroups), dim3(kThreads), s, ev, a);
-      return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2>, tiles_grid, dim3(kThreads), s, ev, a);
-    }
+      break;
+    case Form::kPairTile:
+      if constexpr (kHasPairKernels<T, TILE>)
+        return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2>, tiles_grid, dim3(kThreads), s, ev, a);
+      break;
+    case Form::kLoop:
+      if constexpr (TILE <= 192)
+        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
+      break;
+    case Form::kTile:
+      return launch_kernel(k_sym<T, TILE, GRAM_INPUT>, tiles_grid, dim3(kThreads), s, ev, a);
   }
-  if constexpr (TILE <= 192) {
-    if (use_persistent(TILE, ntri * batch, ktiles))
-      return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
-  }
-  return launch_kernel(k_sym<T, TILE, GRAM_INPUT>, tiles_grid, dim3(kThreads), s, ev, a);
+  return hipErrorInvalidConfiguration;
 }
 
 template <typename T, typename OutT, int TILE, bool CAP>
@@ -299,15 +323,21 @@ hipError_t launch_nt_cap(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, Launch
   const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
   const dim3 flat((unsigned)(per * batch));
   a.batch = (int)batch;
-  if constexpr (kHasPairKernels<T, TILE>) {
-    if (use_pair(TILE, (int)sizeof(T), per * batch))
-      return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP>, flat, dim3(kThreads), s, ev, a);
+  switch (nt_form(TILE, (int)sizeof(T), per * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
+    case Form::kPairTile:
+      if constexpr (kHasPairKernels<T, TILE>)
+        return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP>, flat, dim3(kThreads), s, ev, a);
+      break;
+    case Form::kLoop:
+      if constexpr (TILE <= 192)
+        return launch_kernel(k_nt_loop<T, OutT, TILE, TN, 1, CAP>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
+      break;
+    case Form::kTile:
+      return launch_kernel(k_nt<T, OutT, TILE, TN, 1, CAP>, flat, dim3(kThreads), s, ev, a);
+    case Form::kPairLoop:
+      break;
   }
-  if constexpr (TILE <= 192) {
-    if (use_persistent(TILE, per * batch, a.K / (kRowBytes / (int)sizeof(T))))
-      return launch_kernel(k_nt_loop<T, OutT, TILE, TN, 1, CAP>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
-  }
-  return launch_kernel(k_nt<T, OutT, TILE, TN, 1, CAP>, flat, dim3(kThreads), s, ev, a);
+  return hipErrorInvalidConfiguration;
 }
 
 // Updates with an E term (the standard form) take the kernels that capture
@@ -337,6 +367,7 @@ struct Runner {
   Tracer tr;
 
   T* xbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_x[i]); }
+  int32_t* status() const { return opt ? opt->d_status : nullptr; }
   // Length of a contraction over `real` rows or columns: a whole number of
   // k-tiles (64 16-bit or 32 fp32 elements).
   static int64_t k_extent(int64_t real) { return round_up(real, kRowBytes / (int64_t)sizeof(T)); }
@@ -379,9 +410,25 @@ struct Runner {
     const double flops = n * n * inner * bt;
     double bytes = (L == R ? 1.0 : 2.0) * n * inner * es + n * n * es * (1.0 + (E ? 1.0 : 0.0) + (C2 ? 1.0 : 0.0));
     bytes *= bt;
-    if (gram)
-      return tr.run(NS_KERNEL_GRAM, flops, bytes, [&](LaunchEvents ev) { return launch_sym<T, TILE, true>(a, p.batch, st, ev); });
-    return tr.run(NS_KERNEL_SYM, flops, bytes, [&](LaunchEvents ev) { return launch_sym<T, TILE, false>(a, p.batch, st, ev); });
+    hipError_t e =
+        gram ? tr.run(NS_KERNEL_GRAM, flops, bytes, [&](LaunchEvents ev) { return launch_sym<T, TILE, true>(a, p.batch, st, ev); })
+             : tr.run(NS_KERNEL_SYM, flops, bytes, [&](LaunchEvents ev) { return launch_sym<T, TILE, false>(a, p.batch, st, ev); });
+    if (e != hipSuccess) return e;
+    if ((e = check_state(C)) != hipSuccess) return e;
+    return C2 ? check_state(C2) : hipSuccess;
+  }
+
+  // With a status word, scans a freshly written n x n buffer (all matrices
+  // of the batch, padding included: it is zero) for NaN and Inf.
+  hipError_t check_state(const T* C) const {
+    if (!status()) return hipSuccess;
+    const int64_t count = p.nn_elems;
+    const bool vec = (count * (int64_t)sizeof(T)) % 16 == 0;
+    const int64_t want = (count * p.batch + 4095) / 4096;  // about 16 elements per thread
+    const unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>((want + p.batch - 1) / p.batch, 1024));
+    hipLaunchKernelGGL(k_check_finite<T>, dim3(gx, (unsigned)p.batch), dim3(kStageThreads), 0, st, C, count,
+                       p.nn_elems, vec ? 1 : 0, status(), (int32_t)(NS_ERR_NONFINITE | NS_STATUS_AT_STATE));
+    return hipGetLastError();
   }
 
   // Y = alpha * X_in + B X_in into X_out and X_out^T (E omitted when alpha
@@ -416,7 +463,8 @@ struct Runner {
     a.alpha = alpha;
     a.gamma = 1.f;
     a.out_scale = 1.f;
-    a.d_status = nullptr;
+    a.d_status = status();
+    a.status_bits = NS_ERR_NONFINITE | NS_STATUS_AT_ITERATE;
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (3.0 + (with_e ? 1.0 : 0.0)));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
@@ -454,7 +502,8 @@ struct Runner {
     a.alpha = alpha;
     a.gamma = 1.f;
     a.out_scale = out_scale;
-    a.d_status = opt ? opt->d_status : nullptr;
+    a.d_status = status();
+    a.status_bits = NS_ERR_NONFINITE | NS_STATUS_AT_OUTPUT;
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (1.0 + (with_e ? 1.0 : 0.0)) + n * m * sizeof(IO));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
@@ -474,7 +523,7 @@ struct Runner {
     if (e != hipSuccess) return e;
     float* scales = reinterpret_cast<float*>(ws + p.off_scale);
     hipLaunchKernelGGL(k_scale, dim3((unsigned)p.batch), dim3(kStageThreads), 0, st, partial, p.partials, prescale,
-                       eps, scales);
+                       eps, scales, status(), (int32_t)(NS_ERR_NONFINITE | NS_STATUS_AT_INPUT));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return tr.run(NS_KERNEL_STAGE, 0.0, elems * (sizeof(IO) + 2 * sizeof(T)), [&](LaunchEvents ev) {
       const int bi = (int)(p.n_pad / 64), bj = (int)(p.m_pad / 64);
@@ -552,6 +601,54 @@ struct Runner {
   }
 };
 
+// The kernel builds a call launches, as text (see ns_plan_kernels): one
+// entry per distinct build, in launch order.
+const char* form_name(Form f) {
+  switch (f) {
+    case Form::kTile: return "tile";
+    case Form::kLoop: return "loop";
+    case Form::kPairTile: return "pair";
+    case Form::kPairLoop: return "pairloop";
+  }
+  return "?";
+}
+const char* dtype_name(ns_dtype d) { return d == NS_FP32 ? "f32" : d == NS_FP16 ? "f16" : "bf16"; }
+
+std::string describe_plan(const Plan& p, int steps, uint32_t mask) {
+  const int esz = p.esz;
+  const int64_t per_k = kRowBytes / esz;
+  const int64_t km = round_up(p.m, per_k) / per_k, kn = round_up(p.n, per_k) / per_k;
+  const int64_t nt = p.n_pad / p.tile, ntri = nt * (nt + 1) / 2 * p.batch;
+  const int64_t nt_tiles = nt * (p.m_pad / p.tile_n) * p.batch;
+  const std::string T = dtype_name(p.internal), IO = dtype_name(p.io), E = std::to_string(p.tile);
+  // Updates with an E term capture it from LDS where the tile has the
+  // registers (16-bit, edges up to 192), else read it from global memory.
+  const std::string e_term = esz == 2 && p.tile <= 192 ? ",E" : ",Eg";
+  std::vector<std::string> seen;
+  std::string out;
+  auto add = [&](const std::string& v) {
+    if (std::find(seen.begin(), seen.end(), v) != seen.end()) return;
+    seen.push_back(v);
+    out += (out.empty() ? "" : " ") + v;
+  };
+  add("sumsq<" + IO + ">");
+  add("stage<" + IO + "," + T + ">");
+  const std::string xxt = "xxt<" + T + "," + E + "," + form_name(sym_form(p.tile, esz, ntri, km)) + ">";
+  const std::string nn = "nn<" + T + "," + E + "," + form_name(sym_form(p.tile, esz, ntri, kn)) + ">";
+  const std::string upd = std::string(form_name(nt_form(p.tile, esz, nt_tiles, kn)));
+  add(xxt);
+  add(nn);
+  if (p.mode == NS_STANDARD) {
+    if (steps > 1) add("upd<" + T + "," + T + "," + E + "," + upd + e_term + ">");
+    add("out<" + T + "," + IO + "," + E + "," + upd + e_term + ">");
+  } else {
+    for (int k = 2; k <= steps; ++k)
+      if ((mask >> k) & 1u) add("upd<" + T + "," + T + "," + E + "," + upd + ",noE>");
+    add("out<" + T + "," + IO + "," + E + "," + upd + ",noE>");
+  }
+  return out;
+}
+
 // Where a call reads its input and writes its result.
 struct IoSpec {
   void* in;
@@ -596,12 +693,8 @@ ns_status run_typed(const Plan& p, const IoSpec& io, int steps, const float* a, 
 template <class F>
 ns_status dispatch_types(const Plan& p, F&& f) {
   if (p.io == NS_FP32) return f.template run<float, float>();
-  if (p.io == NS_BF16) {
-    if (p.internal == NS_FP16) return f.template run<_Float16, __bf16>();
-    return f.template run<__bf16, __bf16>();
-  }
-  if (p.internal == NS_FP16) return f.template run<_Float16, _Float16>();
-  return f.template run<__bf16, _Float16>();
+  if (p.io == NS_BF16) return f.template run<_Float16, __bf16>();
+  return f.template run<_Float16, _Float16>();
 }
 
 struct OrthCall {
@@ -618,21 +711,86 @@ struct OrthCall {
   }
 };
 
+// Largest magnitude each stored quantity of the iteration reaches in exact
+// arithmetic.  Every matrix of both forms is a function of the singular
+// values of X0 (which lie in [0, 1] after the Frobenius scaling), with its
+// entries bounded by its spectral norm, so tracking one singular value s
+// through the steps bounds them all:
+//   standard: A = s^2, b A + c A^2, the new X = p(s) (held as 2^10 X in
+//     16-bit storage);
+//   Gram: from a start or restart with singular value s, R = lambda = s^2,
+//     Z' = b lambda + c lambda^2, Q's eigenvalue (a + Z') Q, V = lambda z,
+//     R <- lambda z^2, and at a restart X <- Q X.
+// The maxima are taken over a grid of s (linear on [0, 1] and logarithmic
+// down to 1e-9, where Q's eigenvalue reaches the product of the a_k); the
+// limits keep a factor of two below each type's largest value for the
+// maxima between grid points (a value that still overflows on the device is
+// reported through the status word).
+struct RangeBound {
+  double x = 0, nn = 0, out = 0;  // X iterates (unscaled), n x n state, result
+};
+
+RangeBound scalar_bounds(int steps, const float* a, const float* b, const float* c, ns_mode mode, uint32_t mask) {
+  RangeBound r;
+  auto upd = [](double& m, double v) { m = std::max(m, fabs(v)); };
+  auto one = [&](double sigma) {
+    if (mode == NS_STANDARD) {
+      double s = sigma;
+      for (int k = 0; k < steps; ++k) {
+        const double A = s * s, B = b[k] * A + c[k] * A * A;
+        upd(r.nn, A);
+        upd(r.nn, B);
+        s = a[k] * s + B * s;
+        if (k + 1 < steps) upd(r.x, s);
+      }
+      upd(r.out, s);
+      return;
+    }
+    double s = sigma, lam = s * s, q = 1.0;
+    bool fresh = true;
+    upd(r.nn, lam);
+    for (int k = 1; k <= steps; ++k) {
+      if (k > 1 && ((mask >> k) & 1u)) {
+        s *= q;
+        upd(r.x, s);
+        lam = s * s;
+        upd(r.nn, lam);
+        q = 1.0;
+        fresh = true;
+      }
+      const double zp = b[k - 1] * lam + c[k - 1] * lam * lam, z = a[k - 1] + zp;
+      upd(r.nn, zp);
+      q = fresh ? z : q * z;
+      upd(r.nn, q);
+      fresh = false;
+      if (k < steps && !((mask >> (k + 1)) & 1u)) {
+        upd(r.nn, lam * z);
+        lam *= z * z;
+        upd(r.nn, lam);
+      }
+    }
+    upd(r.out, q * s);
+  };
+  for (int i = 0; i <= 512; ++i) one(i / 512.0);
+  const double step = 1.1220184543019633;  // 10^(1/20)
+  double sigma = 1e-9;
+  for (int i = 0; i < 180; ++i, sigma *= step) one(sigma);
+  return r;
+}
+
 ns_status check_coefficients(int32_t steps, const float* a, const float* b, const float* c, ns_mode mode,
-                             uint32_t mask, ns_dtype internal) {
+                             uint32_t mask, ns_dtype internal, ns_dtype io) {
   if (steps < 1 || steps > NS_MAX_STEPS || !a || !b || !c) return NS_ERR_INVALID_ARG;
   for (int k = 0; k < steps; ++k)
     if (!isfinite(a[k]) || !isfinite(b[k]) || !isfinite(c[k])) return NS_ERR_INVALID_ARG;
-  if (mode == NS_GRAM && internal != NS_FP32) {
-    // The accumulated Q is a product of factors a_k I + ... whose largest
-    // eigenvalue can reach |a_k| per step; keep it inside fp16 range.
-    double run = 1.0;
-    for (int k = 1; k <= steps; ++k) {
-      if (k > 1 && ((mask >> k) & 1u)) run = 1.0;
-      run *= fabs((double)a[k - 1]);
-      if (run >= 32768.0) return NS_ERR_INVALID_ARG;
-    }
-  }
+  // Stored values stay below half of the storage type's largest finite
+  // value: 2^15 for fp16 (X is held as 2^10 X), 2^127 for fp32; the result
+  // below half of the I/O type's (bf16 shares fp32's range).
+  const RangeBound r = scalar_bounds(steps, a, b, c, mode, mask);
+  const double lim = internal == NS_FP32 ? 0x1p127 : 32768.0;
+  const double xlim = internal == NS_FP32 ? 0x1p127 : 32768.0 / (double)(1 << kPrescaleExp16);
+  const double olim = io == NS_FP16 ? 32768.0 : 0x1p127;
+  if (!(r.nn < lim) || !(r.x < xlim) || !(r.out < olim)) return NS_ERR_INVALID_ARG;
   return NS_OK;
 }
 
@@ -647,7 +805,7 @@ ns_status orthogonalize_impl(void* X, int64_t batch, int64_t rows, int64_t cols,
   if (s != NS_OK) return s;
   if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
   const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
-  if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal)) != NS_OK) return s;
+  if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal, p.io)) != NS_OK) return s;
   if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
   return dispatch_types(p, OrthCall{p, IoSpec{X, ld, bstride, X, ld, bstride, false, 0.f}, steps, a, b, c, opt, ws,
                                     reinterpret_cast<hipStream_t>(stream)});
@@ -706,7 +864,7 @@ ns_status muon_impl(void* W, const void* G, float* M, int64_t batch, int64_t row
   if (s != NS_OK) return s;
   if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
   const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
-  if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal)) != NS_OK) return s;
+  if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal, p.io)) != NS_OK) return s;
   if (!ws || ws_bytes < muon_total(p) || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
   void* U = reinterpret_cast<char*>(ws) + muon_u_offset(p);
   return dispatch_types(p, MuonCall{p, W, U, G, M, ld, bstride, lr, mu, nesterov, steps, a, b, c, opt, ws,
@@ -720,7 +878,7 @@ size_t threshold_ws_bytes() {
 
 template <typename IO>
 ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float lambda, float mult,
-                          float* d_lambda_out, void* ws, hipStream_t st) {
+                          float* d_lambda_out, int32_t* d_status, void* ws, hipStream_t st) {
   char* w = reinterpret_cast<char*>(ws);
   SelectState* state = reinterpret_cast<SelectState*>(w);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + align_up(sizeof(SelectState)));
@@ -763,7 +921,8 @@ ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float 
     }
   }
   hipLaunchKernelGGL((k_clip_split<IO>), dim3(grid), dim3(256), 0, st, m, reinterpret_cast<IO*>(B),
-                     reinterpret_cast<IO*>(O), numel, state, vec_clip);
+                     reinterpret_cast<IO*>(O), numel, state, vec_clip, d_status,
+                     (int32_t)(NS_ERR_NONFINITE | NS_STATUS_AT_SPLIT));
   return hip_status(hipGetLastError());
 }
 
@@ -803,6 +962,19 @@ ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows, int64_t
                             workspace_bytes, stream);
 }
 
+int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode, int32_t steps,
+                        const ns_options* opt, char* buf, size_t len) {
+  Plan p;
+  if (make_plan(rows, cols, batch, dtype, mode, opt, &p) != NS_OK || steps < 1 || steps > NS_MAX_STEPS) return -1;
+  const std::string d = describe_plan(p, steps, opt ? opt->restart_mask : (1u << 4));
+  if (buf && len > 0) {
+    const size_t n = std::min(len - 1, d.size());
+    memcpy(buf, d.data(), n);
+    buf[n] = 0;
+  }
+  return (int64_t)d.size() + 1;
+}
+
 size_t ns_muon_workspace_size(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode,
                               const ns_options* opt) {
   Plan p;
@@ -828,17 +1000,17 @@ size_t ns_soft_threshold_workspace_size(int64_t numel, ns_dtype dtype) {
 }
 
 ns_status ns_soft_threshold_split(const void* M, void* B, void* O, int64_t numel, ns_dtype dtype, float lambda,
-                                  float mult, float* d_lambda_out, void* workspace, size_t workspace_bytes,
-                                  ns_stream_t stream) {
+                                  float mult, float* d_lambda_out, int32_t* d_status, void* workspace,
+                                  size_t workspace_bytes, ns_stream_t stream) {
   if (!M || !B || numel < 1 || numel > kMaxThresholdNumel) return NS_ERR_INVALID_ARG;
   if (isnan(lambda) || (lambda < 0.f && !(isfinite(mult) && mult >= 0.f))) return NS_ERR_INVALID_ARG;
   if (dtype != NS_BF16 && dtype != NS_FP16 && dtype != NS_FP32) return NS_ERR_UNSUPPORTED_DTYPE;
   if (!workspace || workspace_bytes < threshold_ws_bytes() || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return NS_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == NS_BF16) return threshold_typed<__bf16>(M, B, O, numel, lambda, mult, d_lambda_out, workspace, st);
-  if (dtype == NS_FP16) return threshold_typed<_Float16>(M, B, O, numel, lambda, mult, d_lambda_out, workspace, st);
-  return threshold_typed<float>(M, B, O, numel, lambda, mult, d_lambda_out, workspace, st);
+  if (dtype == NS_BF16) return threshold_typed<__bf16>(M, B, O, numel, lambda, mult, d_lambda_out, d_status, workspace, st);
+  if (dtype == NS_FP16) return threshold_typed<_Float16>(M, B, O, numel, lambda, mult, d_lambda_out, d_status, workspace, st);
+  return threshold_typed<float>(M, B, O, numel, lambda, mult, d_lambda_out, d_status, workspace, st);
 }
 
 const char* ns_status_string(ns_status s) {
@@ -848,10 +1020,11 @@ const char* ns_status_string(ns_status s) {
     case NS_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
     case NS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case NS_ERR_HIP: return "HIP runtime error";
+    case NS_ERR_NONFINITE: return "non-finite value produced on the device";
   }
   return "unknown status";
 }
 
-int32_t ns_version(void) { return 200; }
+int32_t ns_version(void) { return 300; }
 
 }  // extern "C"

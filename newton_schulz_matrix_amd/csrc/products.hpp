@@ -18,8 +18,9 @@
 //   * 256 threads = 4 wave64s in a 2 x 2 grid; square block tiles of 128,
 //     192 or 256 (the same edge for both products of a call); each wave owns
 //     a (TM/2) x (TN/2) sub-tile made of 32 x 32 MFMA tiles
-//     (v_mfma_f32_32x32x16_{f16,bf16}; for fp32 operands four
-//     v_mfma_f32_32x32x2_f32 per 16-byte chunk).  The 192 edge exists for
+//     (v_mfma_f32_32x32x16_f16; for fp32 operands four
+//     v_mfma_f32_32x32x2_f32 per 16-byte chunk).  16-bit input of either
+//     type (bf16 or fp16) is multiplied on fp16 operands.  The 192 edge exists for
 //     occupancy: a 4096 x 4096 symmetric product has 136 upper-triangle
 //     tiles of 256 but 253 of 192, for 256 compute units.
 //   * K is consumed in k-tiles of 128 bytes per operand row (64 16-bit or
@@ -44,7 +45,6 @@
 namespace nsk {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -114,9 +114,6 @@ template <typename T> __device__ __forceinline__ void mma_chunk(const uint4& a, 
 
 template <> __device__ __forceinline__ void mma_chunk<_Float16>(const uint4& a, const uint4& b, f32x16& acc) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
-}
-template <> __device__ __forceinline__ void mma_chunk<__bf16>(const uint4& a, const uint4& b, f32x16& acc) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 template <> __device__ __forceinline__ void mma_chunk<float>(const uint4& a, const uint4& b, f32x16& acc) {
   // Lane half h holds k = 4h..4h+3 of this 8-wide k group in both operands;
@@ -536,8 +533,16 @@ struct NTArgs {
   float alpha, gamma, out_scale;
   int accumulate;      // final output only: 0 stores the result; 1: Y <- Y + apply_scale * result
   float apply_scale;
-  int32_t* d_status;
+  int32_t* d_status;    // optional status word: status_bits ORed in on NaN / Inf
+  int32_t status_bits;
 };
+
+// Ors `bits` into the status word once per wave in which some lane saw a
+// bad value.
+__device__ __forceinline__ void report_status(int32_t* d_status, int32_t bits, bool bad) {
+  const unsigned long long any_bad = __ballot(bad);
+  if (any_bad && (int)(threadIdx.x & 63) == __ffsll(any_bad) - 1) atomicOr(d_status, bits);
+}
 
 // The caller's 16-byte chunk `dst` gets `val` (kEC rounded results), or
 // with `acc`, dst + s * val computed in fp32 and rounded once more.
@@ -883,7 +888,9 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
 
   // Phase A: beta*E + gamma*acc, rounded to T, into the LDS tile.  The
   // diagonal of C2 (= C + delta I on real rows) is written here, rounded
-  // once from fp32.
+  // once from fp32.  (Non-finite results are found by a separate scan of
+  // the output when the caller asks for it: a check here slowed the
+  // products down by 7 %, status word or not.)
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int il = wr + fm * 32 + lr;
@@ -1066,7 +1073,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
         v[3] = p.gamma * acc.v[fm][fn][4 * g + 3];
         if (E) v += p.alpha * ep.get(E, p.lde, row0, col0, il, jl, fm, fn, g);
         v *= scale;
-        if (p.final_out && p.d_status) {
+        if (p.d_status) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) bad |= !(fabsf(v[e]) < kRoundsToInf<OutT>);
         }
@@ -1153,10 +1160,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
       }
     }
   }
-  if (p.d_status) {
-    const unsigned long long any_bad = __ballot(bad);
-    if (any_bad && lane == __ffsll(any_bad) - 1) atomicOr(p.d_status, 1);
-  }
+  if (p.d_status) report_status(p.d_status, p.status_bits, bad);
 }
 
 // One work-group per tile on a one-dimensional grid over the tiles of all

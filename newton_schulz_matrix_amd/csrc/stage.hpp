@@ -89,15 +89,19 @@ __global__ void __launch_bounds__(kStageThreads) k_sumsq(const IO* M, int64_t ro
 }
 
 // scale[b] = prescale / (sqrt(sum of the P partials of matrix b) + eps),
-// summed in a fixed order.  One block per matrix.
+// summed in a fixed order.  One block per matrix.  A non-finite sum (NaN or
+// Inf in the input) ORs status_bits into the optional status word.
 __global__ void __launch_bounds__(kStageThreads) k_scale(const double* partial, int P, float prescale, float eps,
-                                                        float* scale) {
+                                                        float* scale, int32_t* d_status, int32_t status_bits) {
   __shared__ double sh[kStageThreads / 64];
   const double* pp = partial + (int64_t)blockIdx.x * P;
   double v = 0.0;
   for (int i = threadIdx.x; i < P; i += kStageThreads) v += pp[i];
   v = block_sum(v, sh);
-  if (threadIdx.x == 0) scale[blockIdx.x] = (float)((double)prescale / (sqrt(v) + (double)eps));
+  if (threadIdx.x == 0) {
+    scale[blockIdx.x] = (float)((double)prescale / (sqrt(v) + (double)eps));
+    if (d_status && !(v < __builtin_huge_val())) atomicOr(d_status, status_bits);
+  }
 }
 
 // Both layouts of the scaled, oriented, zero-padded matrix: X (n_pad x
@@ -161,6 +165,34 @@ __global__ void __launch_bounds__(kStageThreads) k_stage_pair(const IO* M, int64
   }
 }
 
+// Scan of `count` contiguous elements of each of `batch` buffers (batch
+// stride bstride elements) for NaN and Inf: status_bits are ORed into the
+// status word when one is found.  16-byte loads when count, bstride and
+// the base are multiples of 16 bytes.
+template <typename T>
+__global__ void __launch_bounds__(kStageThreads) k_check_finite(const T* p, int64_t count, int64_t bstride,
+                                                               int vec_ok, int32_t* d_status, int32_t status_bits) {
+  const T* a = p + (int64_t)blockIdx.y * bstride;
+  const int64_t tid = (int64_t)blockIdx.x * kStageThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kStageThreads;
+  bool bad = false;
+  int64_t done = 0;
+  if (vec_ok) {
+    constexpr int V = 16 / sizeof(T);
+    const int64_t nv = count / V;
+    const uint4* av = reinterpret_cast<const uint4*>(a);
+    for (int64_t i = tid; i < nv; i += stride) {
+      const uint4 q = av[i];
+      const T* e = reinterpret_cast<const T*>(&q);
+#pragma unroll
+      for (int k = 0; k < V; ++k) bad |= !(fabsf(to_f32<T>(e[k])) < __builtin_inff());
+    }
+    done = nv * V;
+  }
+  for (int64_t i = done + tid; i < count; i += stride) bad |= !(fabsf(to_f32<T>(a[i])) < __builtin_inff());
+  report_status(d_status, status_bits, bad);
+}
+
 // Muon momentum: M <- mu M + G (fp32), U = G + mu M (Nesterov) or M, U
 // rounded to IO and stored contiguously (rows x cols per matrix).  One
 // block per row; 8 consecutive elements per thread, vectorized when rows
@@ -219,14 +251,6 @@ __global__ void __launch_bounds__(kStageThreads) k_momentum(const IO* G, float* 
       for (int k = 0; k < kV && c0 + k < cols; ++k) u[c0 + k] = uo[k];
     }
   }
-}
-
-// Fill n x n (ld) blocks of a batch with zero (used to clear buffers
-// without memset nodes, so that the sequence can be captured in a graph).
-template <typename T>
-__global__ void k_fill_zero(T* p, int64_t count) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = T(0);
 }
 
 }  // namespace nsk

@@ -208,13 +208,19 @@ __device__ __forceinline__ void clip_one(float x, float lam, IO& b, IO& o) {
   o = from_f32<IO>(x - to_f32<IO>(b));
 }
 
+// With a status word, a non-finite lambda, B or O ORs status_bits into it
+// (NaN inputs pass through to B, so they are reported too).
 template <typename IO>
 __global__ void __launch_bounds__(256) k_clip_split(const IO* M, IO* B, IO* O, int64_t numel, const SelectState* st,
-                                                   int vec_ok) {
+                                                   int vec_ok, int32_t* d_status, int32_t status_bits) {
   const float lam = st->lambda;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t done = 0;
+  bool bad = false;
+  auto check = [&](IO b, IO o) {
+    if (d_status) bad |= !(fabsf(to_f32<IO>(b)) < __builtin_inff()) || !(fabsf(to_f32<IO>(o)) < __builtin_inff());
+  };
   if (vec_ok) {
     constexpr int V = 16 / (int)sizeof(IO);
     typedef IO vec_t __attribute__((ext_vector_type(V)));
@@ -226,6 +232,7 @@ __global__ void __launch_bounds__(256) k_clip_split(const IO* M, IO* B, IO* O, i
       for (int j = 0; j < V; ++j) {
         IO bj, oj;
         clip_one<IO>(to_f32<IO>(m[j]), lam, bj, oj);
+        check(bj, oj);
         b[j] = bj;
         o[j] = oj;
       }
@@ -237,8 +244,13 @@ __global__ void __launch_bounds__(256) k_clip_split(const IO* M, IO* B, IO* O, i
   for (int64_t i = done + tid; i < numel; i += stride) {
     IO b, o;
     clip_one<IO>(to_f32<IO>(M[i]), lam, b, o);
+    check(b, o);
     B[i] = b;
     if (O) O[i] = o;
+  }
+  if (d_status) {
+    bad |= !(fabsf(lam) < __builtin_inff());
+    report_status(d_status, status_bits, bad);
   }
 }
 

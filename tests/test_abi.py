@@ -35,7 +35,7 @@ def test_header_declares_the_api():
                  "ns_muon_step", "ns_muon_workspace_size",
                  "ns_soft_threshold_split", "ns_workspace_size",
                  "ns_soft_threshold_workspace_size", "ns_status_string",
-                 "ns_options_default", "ns_version"]:
+                 "ns_options_default", "ns_version", "ns_plan_kernels"]:
         assert want in names
 
 
@@ -43,13 +43,29 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.ns_version() >= 200
+    assert lib.ns_version() >= 300
 
 
-def test_status_strings():
-    for code in range(5):
-        assert B.status_string(code)
+def test_status_strings_and_word_layout():
+    for code in range(6):
+        assert B.status_string(code) != "unknown status"
     assert B.status_string(99) == "unknown status"
+    # The status word keeps the code in its low byte and the place bits
+    # above it, as the header's NS_STATUS_CODE and NS_STATUS_AT_* say.
+    text = open(HEADER).read()
+    assert "NS_ERR_NONFINITE = 5" in text
+    for name, bit in [("NS_STATUS_AT_INPUT", B.STATUS_AT_INPUT),
+                      ("NS_STATUS_AT_STATE", B.STATUS_AT_STATE),
+                      ("NS_STATUS_AT_ITERATE", B.STATUS_AT_ITERATE),
+                      ("NS_STATUS_AT_OUTPUT", B.STATUS_AT_OUTPUT),
+                      ("NS_STATUS_AT_SPLIT", B.STATUS_AT_SPLIT),
+                      ("NS_STATUS_GUARD_RESTART", B.STATUS_GUARD_RESTART)]:
+        m = re.search(r"#define " + name + r" \(1 << (\d+)\)", text)
+        assert m and (1 << int(m.group(1))) == bit, name
+        assert bit > 0xFF
+    word = B.NS_ERR_NONFINITE | B.STATUS_AT_STATE | B.STATUS_AT_OUTPUT
+    assert nsa.status_code(word) == B.NS_ERR_NONFINITE
+    assert nsa.status_code(B.STATUS_GUARD_RESTART) == 0
 
 
 def test_options_defaults():
@@ -152,6 +168,19 @@ def test_workspace_size_rejects_bad_arguments():
     assert lib.ns_workspace_size(8, 8, 1, B.NS_BF16, 0, ctypes.byref(opt)) == 0
 
 
+def test_bf16_products_are_refused():
+    # bf16 operands keep 8 mantissa bits in every stored intermediate and
+    # miss the 1e-2 bar of 16-bit input, so the option is refused for every
+    # input type (the automatic choice is fp16 for 16-bit input).
+    lib = B.lib()
+    opt = B.make_options(internal="bf16")
+    for dt in (B.NS_BF16, B.NS_FP16, B.NS_FP32):
+        assert lib.ns_workspace_size(64, 96, 1, dt, 1, ctypes.byref(opt)) == 0
+    assert _call(opt=opt) == 2
+    assert _call(opt=opt, dtype=B.NS_FP16) == 2
+    assert nsa.plan_kernels(64, 96, dtype=torch.bfloat16)[1] == "stage<bf16,f16>"
+
+
 def _call(ptr=1, rows=8, cols=8, ld=8, dtype=B.NS_BF16, steps=5, abc=None,
           mode=B.NS_STANDARD, opt=None, ws=256, ws_bytes=1 << 40):
     a, b, c = B._coefficients(abc or B.TUNED_ABC, max(steps, 1))
@@ -176,13 +205,72 @@ def test_orthogonalize_argument_checks():
     assert _call(abc=(float("nan"), 1.0, 1.0)) == inv
     opt = B.make_options(eps=-1.0)
     assert _call(opt=opt) == inv
-    # Gram with fp16 state: a^k must stay below 2^15 between restarts.
+    # Gram with fp16 state: Q reaches the product of the a_k between
+    # restarts, which must stay below 2^15 (3.4445^8 < 2^15 < 3.4445^9).
     opt = B.make_options(restart_mask=0)
     assert _call(steps=9, mode=B.NS_GRAM, opt=opt) == inv
+    assert _call(steps=8, mode=B.NS_GRAM, opt=opt, ws_bytes=16) == wsp
     opt = B.make_options(restart_mask=(1 << 4) | (1 << 7))
     # 3 + 3 + 3 steps between restarts: 3.4445^3 < 2^15, but the check runs
     # before the workspace check, which is what fails here.
     assert _call(steps=9, mode=B.NS_GRAM, opt=opt, ws_bytes=16) == wsp
+
+
+def test_coefficient_range_check_follows_the_scalar_map():
+    # Schedules whose product of |a_k| is small but whose other stored
+    # quantities leave the fp16 range: Z' = b R + c R^2 reaches |c| at
+    # s = 1, V = R Z and R <- R Z^2 grow with z^2, and the standard form's
+    # X (held as 2^10 X) reaches p(1) = a + b + c.
+    inv, wsp = 1, 3
+    gram, std = B.NS_GRAM, B.NS_STANDARD
+    opt0 = B.make_options(restart_mask=0)
+    assert _call(steps=1, abc=(1.0, 0.0, 40000.0), mode=gram, opt=opt0) == inv
+    assert _call(steps=1, abc=(1.0, 0.0, 20000.0), mode=gram, opt=opt0, ws_bytes=16) == wsp
+    # R <- R z^2 after step 1 with z = 200 at s = 1: 4e4 (the product of
+    # the a_k is only 200); step 2 multiplies by 1.
+    assert _call(steps=2, abc=[(200.0, 0.0, 0.0), (1.0, 0.0, 0.0)], mode=gram,
+                 opt=opt0) == inv
+    assert _call(steps=2, abc=[(100.0, 0.0, 0.0), (1.0, 0.0, 0.0)], mode=gram,
+                 opt=opt0, ws_bytes=16) == wsp
+    # Standard form: the next X is p(s) <= 40; held as 2^10 X that is 4e4.
+    assert _call(steps=2, abc=(40.0, 0.0, 0.0), mode=std) == inv
+    assert _call(steps=2, abc=(20.0, 0.0, 0.0), mode=std, ws_bytes=16) == wsp
+    # fp32 products have fp32's range.
+    assert _call(steps=2, abc=(40.0, 0.0, 0.0), mode=std, dtype=B.NS_FP32,
+                 ws_bytes=16) == wsp
+    # The result of a one-step schedule is p(s) <= 40000: above 2^15 in fp16
+    # I/O, inside bf16's and fp32's range.
+    one = (40000.0, 0.0, 0.0)
+    assert _call(steps=1, abc=one, mode=std, dtype=B.NS_FP16) == inv
+    assert _call(steps=1, abc=one, mode=std, dtype=B.NS_BF16, ws_bytes=16) == wsp
+    assert _call(steps=1, abc=one, mode=std, dtype=B.NS_FP32, ws_bytes=16) == wsp
+    # The tuned and classic triples, and every per-shape ROOT schedule in
+    # the coefficient table, pass in both forms.
+    for abc in (B.TUNED_ABC, (2.0, -1.5, 0.5)):
+        for mode in (std, gram):
+            assert _call(abc=abc, mode=mode, ws_bytes=16) == wsp
+    from newton_schulz_matrix_amd import coeffs
+    for entry in coeffs.load_table().values():
+        sched = [tuple(t) for t in entry["coefficients"]]
+        for mode in (std, gram):
+            assert _call(steps=len(sched), abc=sched, mode=mode, ws_bytes=16) == wsp
+
+
+def test_plan_kernels_names_the_builds():
+    ks = nsa.plan_kernels(4096, 14336, 1, torch.bfloat16, "gram")
+    assert ks == ["sumsq<bf16>", "stage<bf16,f16>", "xxt<f16,192,tile>",
+                  "nn<f16,192,tile>", "upd<f16,f16,192,tile,noE>",
+                  "out<f16,bf16,192,tile,noE>"]
+    ks = nsa.plan_kernels(2048, 1408, 128, torch.bfloat16, "standard")
+    assert ks[2:] == ["xxt<f16,128,pairloop>", "nn<f16,128,pairloop>",
+                      "upd<f16,f16,128,pair,E>", "out<f16,bf16,128,pair,E>"]
+    # The naive Gram form has no restart update; fp32 takes 128 tiles and
+    # reads the a X term from global memory.
+    ks = nsa.plan_kernels(300, 200, 1, torch.float32, "gram", restart_mask=0)
+    assert not any(k.startswith("upd<") for k in ks)
+    ks = nsa.plan_kernels(300, 200, 1, torch.float32, "standard")
+    assert "upd<f32,f32,128,tile,Eg>" in ks
+    assert B.lib().ns_plan_kernels(0, 5, 1, 0, 0, 5, None, None, 0) == -1
 
 
 def test_batched_argument_checks():
@@ -212,7 +300,7 @@ def test_soft_threshold_argument_checks():
         return lib.ns_soft_threshold_split(
             ctypes.c_void_p(a["M"]), ctypes.c_void_p(a["Bp"]),
             ctypes.c_void_p(a["O"]), a["numel"], a["dt"], a["lam"], a["mult"],
-            None, ctypes.c_void_p(a["ws"]), a["wsb"], None)
+            None, None, ctypes.c_void_p(a["ws"]), a["wsb"], None)
     assert call(M=0) == 1
     assert call(numel=0) == 1
     # Bin counts are 32-bit: 2^32 elements and more are refused.

@@ -94,39 +94,24 @@ def test_parity_config1_fp32_both_forms():
         assert err < 1e-4
 
 
-@pytest.mark.parametrize("internal", ["fp16", "bf16"])
-def test_parity_gram_restart_schedules(internal):
+def test_parity_gram_restart_schedules():
     # Ill-conditioned input (column scales down to 1e-3).  The Gram-NS article
     # ("Stability challenges and solutions") reports that the naive Gram
     # iteration is unstable in half precision and that restarting fixes it:
     # with fp16 products every restarted schedule meets the 1e-2 bar and the
-    # naive one is the worst of the three.
+    # naive one is the worst of the four.
     m = workloads.column_scaled(384, 1000, seed=21, dtype="bf16")
     m64 = m.double().numpy()
     errs = {}
     masks = (0, 1 << 3, 1 << 4, (1 << 2) | (1 << 4))
     for mask in masks:
         ref = _oracle(m64, "gram", mask=mask)
-        errs[mask] = _rel(_run(m, "gram", mask=mask, internal=internal), ref)
-    print(f"internal {internal}: " +
-          ", ".join(f"mask {k:#x}: {v:.3e}" for k, v in errs.items()))
+        errs[mask] = _rel(_run(m, "gram", mask=mask), ref)
+    print(", ".join(f"mask {k:#x}: {v:.3e}" for k, v in errs.items()))
     restarted = [errs[k] for k in masks[1:]]
     assert errs[0] > max(restarted)
-    if internal == "fp16":
-        assert errs[0] < 5e-2
-        assert max(restarted) < 1e-2
-    else:
-        # bf16 products keep 8 mantissa bits: the restart still helps, but
-        # the 1e-2 bar is for the default fp16 products.
-        assert errs[(1 << 2) | (1 << 4)] < 3e-2
-
-
-def test_parity_bf16_internal_standard():
-    m = workloads.gaussian((256, 1024), seed=22, dtype="bf16")
-    err = _rel(_run(m, "standard", internal="bf16"),
-               _oracle(m.double().numpy(), "standard"))
-    print(f"bf16 internal standard: {err:.3e}")
-    assert err < 1.5e-2
+    assert errs[0] < 5e-2
+    assert max(restarted) < 1e-2
 
 
 def test_parity_per_step_coefficients_and_steps():
@@ -162,18 +147,52 @@ def test_zero_matrix_gives_zero():
         assert torch.count_nonzero(x).item() == 0
 
 
-def test_nonfinite_status_flag():
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_nonfinite_status_word(mode, bad):
+    # A clean call leaves the word clear.  A NaN or Inf in the input makes
+    # the norm non-finite (NS_STATUS_AT_INPUT); it then spreads through
+    # every product, so the n x n epilogues (R, Z', Q, V / A, b A + c A^2)
+    # report NS_STATUS_AT_STATE and the final one NS_STATUS_AT_OUTPUT, each
+    # with the code NS_ERR_NONFINITE in the low byte.
+    from newton_schulz_matrix_amd import _binding as B
     dev = _dev()
     st = torch.zeros(1, dtype=torch.int32, device=dev)
     x = workloads.gaussian((64, 96), seed=26).to(dev)
-    nsa.orthogonalize(x, status=st)
+    nsa.orthogonalize(x, mode=mode, status=st)
     torch.cuda.synchronize()
     assert st.item() == 0
     x = workloads.gaussian((64, 96), seed=26).to(dev)
-    x[3, 5] = float("nan")
-    nsa.orthogonalize(x, status=st)
+    x[3, 5] = bad
+    nsa.orthogonalize(x, mode=mode, status=st)
     torch.cuda.synchronize()
-    assert st.item() == 1
+    word = st.item()
+    assert nsa.status_code(word) == B.NS_ERR_NONFINITE
+    for bit in (B.STATUS_AT_INPUT, B.STATUS_AT_STATE, B.STATUS_AT_OUTPUT):
+        assert word & bit, hex(word)
+    assert not word & (B.STATUS_AT_SPLIT | B.STATUS_GUARD_RESTART)
+    if mode == "standard":
+        assert word & B.STATUS_AT_ITERATE
+    # Without a status word the same call runs the same kernels unchecked.
+    y = workloads.gaussian((64, 96), seed=26).to(dev)
+    y[3, 5] = bad
+    nsa.orthogonalize(y, mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.isnan(x), torch.isnan(y))
+
+
+def test_binding_rejects_mismatched_buffers():
+    # Checked in Python before any call into the library.
+    dev = _dev()
+    m = torch.zeros(64, 96, dtype=torch.bfloat16, device=dev)
+    for out_b in (torch.zeros(64, 96, dtype=torch.float16, device=dev),
+                  torch.zeros(64, 95, dtype=torch.bfloat16, device=dev),
+                  torch.zeros(96, 128, dtype=torch.bfloat16, device=dev)[:, :64].t(),
+                  torch.zeros(64, 96, dtype=torch.bfloat16)):
+        with pytest.raises(ValueError):
+            nsa.soft_threshold_split(m, out_b=out_b)
+    with pytest.raises(ValueError):
+        nsa.orthogonalize(m, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
 
 
 def test_exact_symmetry_and_orientation():
@@ -216,14 +235,12 @@ def test_parity_forced_tile(tile, shape, mode):
 
 
 @pytest.mark.parametrize("tile", [128, 192, 256])
-def test_forced_tile_fp16_input_bf16_products(tile):
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+def test_forced_tile_fp16_input(tile, mode):
     m = workloads.gaussian((520, 900), seed=42, dtype="fp16")
-    err = _rel(_run(m, "gram", internal="bf16", tile=tile),
-               _oracle(m.double().numpy(), "gram"))
-    print(f"fp16 in, bf16 products, tile {tile}: rel err {err:.3e}")
-    # bf16 products keep 8 mantissa bits, so the bar is looser than for fp16
-    # products; a tile indexing mistake gives errors of order one.
-    assert err < 3e-2
+    err = _rel(_run(m, mode, tile=tile), _oracle(m.double().numpy(), mode))
+    print(f"fp16 in, tile {tile}, {mode}: rel err {err:.3e}")
+    assert err < 1e-2
 
 
 # ---------------------------------------------------------------------------
@@ -285,27 +302,38 @@ def test_soft_threshold_matches_oracle(dtype, numel_shape):
     dev = _dev()
     m = workloads.student_t(numel_shape, seed=29, dtype=dtype)
     m64 = m.double().numpy()
-    b_ref, o_ref, lam_ref = oracle.soft_threshold_split(m64)
     lam_out = torch.zeros(1, dtype=torch.float32, device=dev)
-    b, o = nsa.soft_threshold_split(m.to(dev), lambda_out=lam_out)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    b, o = nsa.soft_threshold_split(m.to(dev), lambda_out=lam_out, status=st)
     torch.cuda.synchronize()
+    assert st.item() == 0
     lam = lam_out.item()
-    # The median is an order statistic of the stored values: exact.
+    # The median is an order statistic of the stored values (exact), and
+    # lambda is 3 * median rounded once to fp32.
     med = oracle.lower_median_abs(m64)
-    assert lam == np.float32(3.0 * med) or lam == pytest.approx(3.0 * med,
-                                                                rel=1e-7)
+    assert lam == float(np.float32(3.0 * med))
     b = b.double().cpu().numpy()
     o = o.double().cpu().numpy()
-    # Which entries are clipped: exact.
-    assert np.array_equal(np.abs(b_ref) >= lam_ref, np.abs(m64) >= lam_ref)
-    clipped_ref = np.abs(m64) > lam_ref
-    assert np.array_equal(o_ref != 0, clipped_ref)
-    assert np.array_equal(b[~clipped_ref], m64[~clipped_ref])
-    # Clipped entries hold lambda rounded to the storage type; O within one
-    # storage ulp of the exact outlier.
+    # Every clip decision, exactly: the oracle's split with the device's
+    # lambda, B rounded to the storage type, equals the device's B.
+    b_ref, o_ref, _ = oracle.soft_threshold_split(m64, lam=lam)
+    b_ref16 = workloads.round_to(b_ref, dtype).double().numpy()
+    assert np.array_equal(b, b_ref16)
+    # O = M - B within one storage ulp of the exact outlier.
     ulp = {"bf16": 2.0 ** -7, "fp16": 2.0 ** -10, "fp32": 2.0 ** -23}[dtype]
-    assert np.all(np.abs(np.abs(b[clipped_ref]) - lam_ref) <= ulp * lam_ref)
-    assert np.all(np.abs(o - o_ref) <= ulp * (np.abs(o_ref) + lam_ref))
+    assert np.all(np.abs(o - o_ref) <= ulp * (np.abs(o_ref) + lam))
+
+
+def test_soft_threshold_status_word():
+    from newton_schulz_matrix_amd import _binding as B
+    dev = _dev()
+    m = workloads.student_t((64, 96), seed=33, dtype="bf16").to(dev)
+    m[1, 2] = float("nan")
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    b, _ = nsa.soft_threshold_split(m, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == B.NS_ERR_NONFINITE | B.STATUS_AT_SPLIT
+    assert torch.isnan(b[1, 2]) and torch.isfinite(b).sum() == b.numel() - 1
 
 
 def test_soft_threshold_explicit_lambda_and_in_place():
