@@ -207,6 +207,32 @@ ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows,
                                    ns_stream_t stream);
 
 /*
+ * ns_orthogonalize_batched without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc).  It calls no allocating routine: its
+ * buffers live in a device array of ns_static_scratch_bytes() bytes (64 MiB)
+ * that the library holds on every device it runs on until the process
+ * ends.  A call whose ns_workspace_size(...) exceeds that returns
+ * NS_ERR_WORKSPACE and enqueues nothing; it fits matrices up to about
+ * 1024 x 4096 (16-bit input), or batches of the same total size.  Results
+ * equal ns_orthogonalize_batched's bit for bit (same kernels).  Nothing in
+ * the array needs to start at zero; every call overwrites what it reads.
+ * All calls on one device share the one array: calls that overlap on one
+ * device (different streams, or threads) race and must be ordered by the
+ * caller.  batch = 1 with batch_stride = rows * ld is a single matrix.
+ * NS_ERR_HIP if the runtime cannot give the array's device address.
+ */
+size_t ns_static_scratch_bytes(void);
+
+ns_status ns_orthogonalize_static(void* X, int64_t batch, int64_t rows,
+                                  int64_t cols, int64_t ld,
+                                  int64_t batch_stride, ns_dtype dtype,
+                                  int32_t steps, const float* a,
+                                  const float* b, const float* c,
+                                  ns_mode mode, const ns_options* opt,
+                                  ns_stream_t stream);
+
+/*
  * ROOT soft-threshold split (ROOT optimizer summary on reportify.cn,
  * "technical innovations of ROOT"): M = B + O with
  *

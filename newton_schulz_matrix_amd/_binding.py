@@ -128,6 +128,17 @@ _SIGNATURES = {
                       ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                       ctypes.POINTER(Options), ctypes.c_void_p,
                       ctypes.c_size_t, ctypes.c_void_p]),
+    "ns_static_scratch_bytes": (ctypes.c_size_t, []),
+    "ns_orthogonalize_static": (ctypes.c_int,
+                                [ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int, ctypes.c_int32,
+                                 ctypes.POINTER(ctypes.c_float),
+                                 ctypes.POINTER(ctypes.c_float),
+                                 ctypes.POINTER(ctypes.c_float),
+                                 ctypes.c_int, ctypes.POINTER(Options),
+                                 ctypes.c_void_p]),
     "ns_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ns_version": (ctypes.c_int32, []),
 }
@@ -323,6 +334,29 @@ def orthogonalize_batched(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
         steps, a, b, c, _MODE_CODE[mode], ctypes.byref(opt),
         ctypes.c_void_p(wptr), wbytes, _stream_handle(x.device))
     _check(st, "ns_orthogonalize_batched")
+    return x
+
+
+def orthogonalize_static(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
+                         mode: str = "gram", restart_mask: int = 1 << 4,
+                         eps: float = 1e-7, internal: Optional[str] = None,
+                         status: Optional[torch.Tensor] = None,
+                         tile: int = 0) -> torch.Tensor:
+    """Orthogonalize a [rows, cols] or [E, rows, cols] device tensor in place
+    with the library's own device scratch (no allocation at all)."""
+    batched = x.dim() == 3
+    _check_matrix(x, 3 if batched else 2)
+    batch = x.shape[0] if batched else 1
+    rows, cols = x.shape[-2], x.shape[-1]
+    ld = x.stride(-2) if rows > 1 else cols
+    bstride = x.stride(0) if batched and batch > 1 else rows * ld
+    opt = make_options(restart_mask, eps, internal, status, None, tile)
+    a, b, c = _coefficients(abc, steps)
+    st = lib().ns_orthogonalize_static(
+        ctypes.c_void_p(x.data_ptr()), batch, rows, cols, ld, bstride,
+        dtype_code(x.dtype), steps, a, b, c, _MODE_CODE[mode],
+        ctypes.byref(opt), _stream_handle(x.device))
+    _check(st, "ns_orthogonalize_static")
     return x
 
 

@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 #include <stdint.h>
@@ -926,6 +927,30 @@ ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float 
   return hip_status(hipGetLastError());
 }
 
+// Scratch of ns_orthogonalize_static: one array per device, allocated when
+// the code object is loaded and held until the process ends.  Host code
+// never uses its name as an address: scratch_ptr() asks the runtime for the
+// current device's copy once and keeps it.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch, or nullptr when the runtime cannot give it.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -973,6 +998,21 @@ int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtyp
     buf[n] = 0;
   }
   return (int64_t)d.size() + 1;
+}
+
+size_t ns_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+ns_status ns_orthogonalize_static(void* X, int64_t batch, int64_t rows, int64_t cols, int64_t ld, int64_t batch_stride,
+                                  ns_dtype dtype, int32_t steps, const float* a, const float* b, const float* c,
+                                  ns_mode mode, const ns_options* opt, ns_stream_t stream) {
+  Plan p;
+  ns_status s = make_plan(rows, cols, batch, dtype, mode, opt, &p);
+  if (s != NS_OK) return s;
+  if (p.total > kStaticScratchBytes) return NS_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) return NS_ERR_HIP;
+  return orthogonalize_impl(X, batch, rows, cols, ld, batch_stride, dtype, steps, a, b, c, mode, opt, ws,
+                            kStaticScratchBytes, stream);
 }
 
 size_t ns_muon_workspace_size(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode,
