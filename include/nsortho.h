@@ -74,6 +74,8 @@ typedef enum {
 #define NS_STATUS_AT_OUTPUT (1 << 11)  /* the result written to the caller's matrix */
 #define NS_STATUS_AT_SPLIT (1 << 12)   /* soft-threshold split: lambda, B or O */
 #define NS_STATUS_GUARD_RESTART (1 << 16)
+/* With NS_STATUS_GUARD_RESTART: the guard restarted before step k, 2 <= k <= 16. */
+#define NS_STATUS_GUARD_STEP(k) ((int32_t)(1u << (15 + (k))))
 
 typedef enum { NS_BF16 = 0, NS_FP16 = 1, NS_FP32 = 2 } ns_dtype;
 
@@ -140,6 +142,19 @@ typedef struct ns_options {
    * 256 for 16-bit products only).  Results do not depend on it beyond
    * fp32 accumulation order; it changes the workspace size. */
   int32_t tile;
+  /* Gram form only: restarts on demand (the Gram-NS article's restart,
+   * "Stability challenges and solutions", triggered by the state instead of
+   * a fixed step).  0 (default) = off.  theta > 0: after step k forms Q, a
+   * restart before step k + 1 is scheduled, matrix by matrix and on the
+   * device, when max_i |Q_ii| * |a_{k+1}| > theta, or when a diagonal entry
+   * of R is negative or not finite.  Q's eigenvalue in the directions of
+   * the smallest singular values grows like the product of the a_j since
+   * the last restart, and its fp16 rounding error with it; 100 restarts an
+   * ill-conditioned input where the fixed schedule does and lets a
+   * well-conditioned one run without a restart.  Restarts of restart_mask
+   * still happen.  Each on-demand restart ORs NS_STATUS_GUARD_RESTART |
+   * NS_STATUS_GUARD_STEP(k) into the status word.  Must be finite. */
+  float guard_threshold;
 } ns_options;
 
 /* Fill *opt with the defaults above. */

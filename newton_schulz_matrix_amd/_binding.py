@@ -66,7 +66,8 @@ class Options(ctypes.Structure):
                 ("internal", ctypes.c_int32),
                 ("d_status", ctypes.c_void_p),
                 ("trace", ctypes.POINTER(Trace)),
-                ("tile", ctypes.c_int32)]
+                ("tile", ctypes.c_int32),
+                ("guard_threshold", ctypes.c_float)]
 
 
 KERNEL_KINDS = ("norm", "stage", "gram", "sym", "update", "threshold",
@@ -194,10 +195,12 @@ def dtype_code(dtype: torch.dtype) -> int:
 def make_options(restart_mask: int = 1 << 4, eps: float = 1e-7,
                  internal: Optional[str] = None,
                  status: Optional[torch.Tensor] = None,
-                 trace: Optional[Trace] = None, tile: int = 0) -> Options:
+                 trace: Optional[Trace] = None, tile: int = 0,
+                 guard: float = 0.0) -> Options:
     opt = Options()
     lib().ns_options_default(ctypes.byref(opt))
     opt.tile = int(tile)
+    opt.guard_threshold = float(guard)
     opt.restart_mask = int(restart_mask)
     opt.eps = float(eps)
     opt.internal = _INTERNAL_CODE[internal]
@@ -285,16 +288,19 @@ def orthogonalize(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
                   eps: float = 1e-7, internal: Optional[str] = None,
                   status: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None,
-                  trace: Optional[Trace] = None, tile: int = 0) -> torch.Tensor:
+                  trace: Optional[Trace] = None, tile: int = 0,
+                  guard: float = 0.0) -> torch.Tensor:
     """Orthogonalize a 2-D device matrix in place; returns it.
 
     ``tile`` forces the products' tile edge (128, 192 or 256; 0 = automatic).
+    ``guard`` > 0 turns on restarts on demand (Gram form) with that
+    threshold (see ns_options.guard_threshold; 100 is the tested value).
     """
     _check_matrix(x, 2)
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
     code = dtype_code(x.dtype)
-    opt = make_options(restart_mask, eps, internal, status, trace, tile)
+    opt = make_options(restart_mask, eps, internal, status, trace, tile, guard)
     need = int(lib().ns_workspace_size(rows, cols, 1, code, _MODE_CODE[mode],
                                        ctypes.byref(opt)))
     if need == 0:
@@ -315,14 +321,14 @@ def orthogonalize_batched(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
                           status: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None,
                           trace: Optional[Trace] = None,
-                          tile: int = 0) -> torch.Tensor:
+                          tile: int = 0, guard: float = 0.0) -> torch.Tensor:
     """Orthogonalize each x[e] of a [E, rows, cols] device tensor in place."""
     _check_matrix(x, 3)
     batch, rows, cols = x.shape
     ld = x.stride(1) if rows > 1 else cols
     bstride = x.stride(0) if batch > 1 else rows * ld
     code = dtype_code(x.dtype)
-    opt = make_options(restart_mask, eps, internal, status, trace, tile)
+    opt = make_options(restart_mask, eps, internal, status, trace, tile, guard)
     need = int(lib().ns_workspace_size(rows, cols, batch, code,
                                        _MODE_CODE[mode], ctypes.byref(opt)))
     if need == 0:
@@ -341,7 +347,7 @@ def orthogonalize_static(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
                          mode: str = "gram", restart_mask: int = 1 << 4,
                          eps: float = 1e-7, internal: Optional[str] = None,
                          status: Optional[torch.Tensor] = None,
-                         tile: int = 0) -> torch.Tensor:
+                         tile: int = 0, guard: float = 0.0) -> torch.Tensor:
     """Orthogonalize a [rows, cols] or [E, rows, cols] device tensor in place
     with the library's own device scratch (no allocation at all)."""
     batched = x.dim() == 3
@@ -350,7 +356,7 @@ def orthogonalize_static(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
     rows, cols = x.shape[-2], x.shape[-1]
     ld = x.stride(-2) if rows > 1 else cols
     bstride = x.stride(0) if batched and batch > 1 else rows * ld
-    opt = make_options(restart_mask, eps, internal, status, None, tile)
+    opt = make_options(restart_mask, eps, internal, status, None, tile, guard)
     a, b, c = _coefficients(abc, steps)
     st = lib().ns_orthogonalize_static(
         ctypes.c_void_p(x.data_ptr()), batch, rows, cols, ld, bstride,
@@ -366,7 +372,8 @@ def muon_step(w: torch.Tensor, g: torch.Tensor, m: torch.Tensor, lr: float,
               eps: float = 1e-7, internal: Optional[str] = None,
               status: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None,
-              trace: Optional[Trace] = None, tile: int = 0) -> torch.Tensor:
+              trace: Optional[Trace] = None, tile: int = 0,
+              guard: float = 0.0) -> torch.Tensor:
     """One Muon step, in place: M <- mu M + G; W <- W - lr NS(G + mu M).
 
     ``w`` and ``g``: [rows, cols] or [E, rows, cols] device tensors of the
@@ -389,7 +396,7 @@ def muon_step(w: torch.Tensor, g: torch.Tensor, m: torch.Tensor, lr: float,
     ld = w.stride(-2) if rows > 1 else cols
     bstride = w.stride(0) if batched and batch > 1 else rows * ld
     code = dtype_code(w.dtype)
-    opt = make_options(restart_mask, eps, internal, status, trace, tile)
+    opt = make_options(restart_mask, eps, internal, status, trace, tile, guard)
     need = int(lib().ns_muon_workspace_size(rows, cols, batch, code,
                                             _MODE_CODE[mode],
                                             ctypes.byref(opt)))

@@ -22,6 +22,9 @@ using namespace nsk;
 namespace {
 
 constexpr size_t kAlign = 256;
+// Per-matrix flags of the guarded Gram iteration: X buffer selector and one
+// restart flag per step.
+constexpr int kFlagStride = NS_MAX_STEPS + 2;
 constexpr int kPrescaleExp16 = 10;  // X is held as 2^10 * X in 16-bit storage
 constexpr int kMaxPartials = 1024;
 
@@ -43,7 +46,7 @@ struct Plan {
   int partials = 1;
   int nn_count = 2;
   int64_t x_elems = 0, nn_elems = 0;
-  size_t off_partial = 0, off_scale = 0, off_x[2] = {0, 0}, off_xt[2] = {0, 0}, off_nn[4] = {0, 0, 0, 0};
+  size_t off_partial = 0, off_scale = 0, off_flags = 0, off_x[2] = {0, 0}, off_xt[2] = {0, 0}, off_nn[4] = {0, 0, 0, 0};
   size_t total = 0;
 };
 
@@ -197,6 +200,8 @@ ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype io, ns_m
   off = align_up(off + (size_t)batch * p->partials * sizeof(double));
   p->off_scale = off;
   off = align_up(off + (size_t)batch * sizeof(float));
+  p->off_flags = off;
+  off = align_up(off + (size_t)batch * kFlagStride * sizeof(int32_t));
   for (int i = 0; i < 2; ++i) {
     p->off_x[i] = off;
     off = align_up(off + (size_t)batch * p->x_elems * p->esz);
@@ -293,8 +298,8 @@ Form nt_form(int edge, int esz, int64_t tiles, int64_t ktiles) {
   return Form::kTile;
 }
 
-template <typename T, int TILE, bool GRAM_INPUT>
-hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+template <typename T, int TILE, bool GRAM_INPUT, bool GUARD>
+hipError_t launch_sym_g(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
   const int64_t ntri = (int64_t)a.tiles * (a.tiles + 1) / 2;
   const int ktiles = a.K / (kRowBytes / (int)sizeof(T));
   const dim3 tiles_grid((unsigned)ntri, (unsigned)batch);
@@ -302,24 +307,34 @@ hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents e
   switch (sym_form(TILE, (int)sizeof(T), ntri * batch, ktiles)) {
     case Form::kPairLoop:
       if constexpr (kHasPairKernels<T, TILE>)
-        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2>, dim3(2 * kPersistentGroups), dim3(kThreads), s, ev, a);
+        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2, GUARD>, dim3(2 * kPersistentGroups), dim3(kThreads), s,
+                             ev, a);
       break;
     case Form::kPairTile:
       if constexpr (kHasPairKernels<T, TILE>)
-        return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2>, tiles_grid, dim3(kThreads), s, ev, a);
+        return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2, GUARD>, tiles_grid, dim3(kThreads), s, ev, a);
       break;
     case Form::kLoop:
       if constexpr (TILE <= 192)
-        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
+        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 1, GUARD>, dim3(kPersistentGroups), dim3(kThreads), s, ev,
+                             a);
       break;
     case Form::kTile:
-      return launch_kernel(k_sym<T, TILE, GRAM_INPUT>, tiles_grid, dim3(kThreads), s, ev, a);
+      return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 1, GUARD>, tiles_grid, dim3(kThreads), s, ev, a);
   }
   return hipErrorInvalidConfiguration;
 }
 
-template <typename T, typename OutT, int TILE, bool CAP>
-hipError_t launch_nt_cap(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+// Launches that read the guard's device flags take the kernels built for
+// them.
+template <typename T, int TILE, bool GRAM_INPUT>
+hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+  if (a.gate || a.c2_gate || a.xsel) return launch_sym_g<T, TILE, GRAM_INPUT, true>(a, batch, s, ev);
+  return launch_sym_g<T, TILE, GRAM_INPUT, false>(a, batch, s, ev);
+}
+
+template <typename T, typename OutT, int TILE, bool CAP, bool GUARD>
+hipError_t launch_nt_g(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
   constexpr int TN = nn_tile_n(TILE);
   const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
   const dim3 flat((unsigned)(per * batch));
@@ -327,18 +342,24 @@ hipError_t launch_nt_cap(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, Launch
   switch (nt_form(TILE, (int)sizeof(T), per * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
     case Form::kPairTile:
       if constexpr (kHasPairKernels<T, TILE>)
-        return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP>, flat, dim3(kThreads), s, ev, a);
+        return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP, GUARD>, flat, dim3(kThreads), s, ev, a);
       break;
     case Form::kLoop:
       if constexpr (TILE <= 192)
-        return launch_kernel(k_nt_loop<T, OutT, TILE, TN, 1, CAP>, dim3(kPersistentGroups), dim3(kThreads), s, ev, a);
+        return launch_kernel(k_nt_loop<T, OutT, TILE, TN, 1, CAP, GUARD>, dim3(kPersistentGroups), dim3(kThreads), s,
+                             ev, a);
       break;
     case Form::kTile:
-      return launch_kernel(k_nt<T, OutT, TILE, TN, 1, CAP>, flat, dim3(kThreads), s, ev, a);
+      return launch_kernel(k_nt<T, OutT, TILE, TN, 1, CAP, GUARD>, flat, dim3(kThreads), s, ev, a);
     case Form::kPairLoop:
       break;
   }
   return hipErrorInvalidConfiguration;
+}
+
+template <typename T, typename OutT, int TILE, bool CAP>
+hipError_t launch_nt_cap(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+  return launch_nt_g<T, OutT, TILE, CAP, false>(a, batch, s, ev);
 }
 
 // Updates with an E term (the standard form) take the kernels that capture
@@ -346,11 +367,23 @@ hipError_t launch_nt_cap(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, Launch
 // Gram form) and the other tiles take the kernels without the capture.
 template <typename T, typename OutT, int TILE>
 hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
+  // The guarded Gram iteration's updates have no E term.
+  if (a.gate || a.xsel) return a.E ? hipErrorInvalidValue : launch_nt_g<T, OutT, TILE, false, true>(a, batch, s, ev);
   if constexpr (EPrefetch<T, TILE, nn_tile_n(TILE)>::kEnabled) {
     if (a.E) return launch_nt_cap<T, OutT, TILE, true>(a, batch, s, ev);
   }
   return launch_nt_cap<T, OutT, TILE, false>(a, batch, s, ev);
 }
+
+// Device flags a launch of the guarded Gram iteration reads (see SymArgs):
+// compute only where the flag at `gate` equals `want`, write C2 only where
+// the flag at `c2` is set, and take the X buffers through the selector.
+struct Gate {
+  const int32_t* gate = nullptr;
+  int32_t want = 0;
+  const int32_t* c2 = nullptr;
+  bool xsel = false;
+};
 
 // One Newton-Schulz run over a batch, for internal type T and I/O type IO.
 template <typename T, typename IO>
@@ -369,6 +402,7 @@ struct Runner {
 
   T* xbuf(int i) const { return reinterpret_cast<T*>(ws + p.off_x[i]); }
   int32_t* status() const { return opt ? opt->d_status : nullptr; }
+  int32_t* flags() const { return reinterpret_cast<int32_t*>(ws + p.off_flags); }
   // Length of a contraction over `real` rows or columns: a whole number of
   // k-tiles (64 16-bit or 32 fp32 elements).
   static int64_t k_extent(int64_t real) { return round_up(real, kRowBytes / (int64_t)sizeof(T)); }
@@ -380,7 +414,7 @@ struct Runner {
   // (the kernels take E's tile from L's k-tiles).
   template <int TILE>
   hipError_t sym(const T* L, const T* R, int K, int ldk, const T* E, float beta, float gamma, T* C, T* C2,
-                 float delta) const {
+                 float delta, const Gate& g = Gate{}) const {
     if (E && E != L) return hipErrorInvalidValue;
     SymArgs<T> a;
     a.L = L;
@@ -406,6 +440,12 @@ struct Runner {
     a.beta = beta;
     a.gamma = gamma;
     a.delta = delta;
+    a.gate = g.gate;
+    a.gate_want = g.want;
+    a.c2_gate = g.c2;
+    a.xsel = g.xsel ? flags() : nullptr;
+    a.x_alt = xbuf(1) - xbuf(0);
+    a.flag_stride = kFlagStride;
     const double n = (double)p.n, bt = (double)p.batch, es = sizeof(T);
     const double inner = gram ? (double)p.m : n;
     const double flops = n * n * inner * bt;
@@ -435,7 +475,7 @@ struct Runner {
   // Y = alpha * X_in + B X_in into X_out and X_out^T (E omitted when alpha
   // is 0).
   template <int TILE>
-  hipError_t nn_internal(const T* B, int xin, bool with_e, float alpha, int xout) const {
+  hipError_t nn_internal(const T* B, int xin, bool with_e, float alpha, int xout, const Gate& g = Gate{}) const {
     NTArgs<T, T> a;
     a.B = B;
     a.XT = xtbuf(xin);
@@ -466,6 +506,13 @@ struct Runner {
     a.out_scale = 1.f;
     a.d_status = status();
     a.status_bits = NS_ERR_NONFINITE | NS_STATUS_AT_ITERATE;
+    a.gate = g.gate;
+    a.gate_want = g.want;
+    a.xsel = g.xsel ? flags() : nullptr;
+    a.xt_alt = xtbuf(1) - xtbuf(0);
+    a.y_alt = xbuf(1) - xbuf(0);
+    a.yt_alt = xtbuf(1) - xtbuf(0);
+    a.flag_stride = kFlagStride;
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (3.0 + (with_e ? 1.0 : 0.0)));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
@@ -474,7 +521,7 @@ struct Runner {
 
   // The caller's matrix = out_scale * (alpha * X_in + B X_in), oriented back.
   template <int TILE>
-  hipError_t nn_final(const T* B, int xin, bool with_e, float alpha, float out_scale) const {
+  hipError_t nn_final(const T* B, int xin, bool with_e, float alpha, float out_scale, const Gate& g = Gate{}) const {
     NTArgs<T, IO> a;
     a.B = B;
     a.XT = xtbuf(xin);
@@ -505,6 +552,13 @@ struct Runner {
     a.out_scale = out_scale;
     a.d_status = status();
     a.status_bits = NS_ERR_NONFINITE | NS_STATUS_AT_OUTPUT;
+    a.gate = g.gate;
+    a.gate_want = g.want;
+    a.xsel = g.xsel ? flags() : nullptr;
+    a.xt_alt = xtbuf(1) - xtbuf(0);
+    a.y_alt = 0;
+    a.yt_alt = 0;
+    a.flag_stride = kFlagStride;
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (1.0 + (with_e ? 1.0 : 0.0)) + n * m * sizeof(IO));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
@@ -563,6 +617,7 @@ struct Runner {
       }
       return hipSuccess;
     }
+    if (opt && opt->guard_threshold > 0.f) return run_guarded<TILE>(steps, a, b, c, km, kn, mp, np, gram_scale, unscale);
     // Gram form.
     const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
     T* R = nnbuf(0);
@@ -600,6 +655,76 @@ struct Runner {
     }
     return nn_final<TILE>(Qb[qi], xi, false, 0.f, unscale);
   }
+
+  // The Gram form with restarts on demand (ns_options.guard_threshold).
+  // Every step k >= 2 has a possible restart; its kernels are always
+  // enqueued and compute, matrix by matrix, only where the flag "restart
+  // before step k" is set: by the fixed restart mask, or by the detector
+  // after step k - 1.  The kernels on either side of a possible restart are
+  // gated the other way (Q's product, R's update), and the fresh
+  // Q = a I + Z' is written where the restart happened.  A restart writes X
+  // into the other buffer pair; the per-matrix selector tells later
+  // launches which pair holds X.  No host synchronization.
+  template <int TILE>
+  hipError_t run_guarded(int steps, const float* a, const float* b, const float* c, int km, int kn, int mp, int np,
+                         float gram_scale, float unscale) const {
+    const uint32_t mask = opt->restart_mask;
+    const float theta = opt->guard_threshold;
+    int32_t* f = flags();
+    const int nf = (int)p.batch * kFlagStride;
+    hipLaunchKernelGGL(k_guard_init, dim3((nf + 255) / 256), dim3(256), 0, st, f, (int)p.batch, kFlagStride, mask);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    T* R = nnbuf(0);
+    T* Z = nnbuf(1);
+    T* Qb[2] = {nnbuf(2), nnbuf(3)};
+    int qi = 0;  // Qb[qi] holds Q after each step
+    Gate sel;
+    sel.xsel = true;
+    if ((e = sym<TILE>(xbuf(0), xbuf(0), km, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f, sel)) != hipSuccess)
+      return e;
+    for (int k = 1; k <= steps; ++k) {
+      const int32_t* fk = f + k;
+      const float ak = a[k - 1], bk = b[k - 1], ck = c[k - 1];
+      if (k > 1) {
+        Gate rs;
+        rs.gate = fk;
+        rs.want = 1;
+        rs.xsel = true;
+        if ((e = nn_internal<TILE>(Qb[qi], 0, false, 0.f, 1, rs)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_guard_flip, dim3(((unsigned)p.batch + 255) / 256), dim3(256), 0, st, f, (int)p.batch,
+                           kFlagStride, k);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = sym<TILE>(xbuf(0), xbuf(0), km, mp, nullptr, 0.f, gram_scale, R, nullptr, 0.f, rs)) != hipSuccess)
+          return e;
+      }
+      // Z' = b R + c R^2, with the fresh Q = a I + Z' where step k starts
+      // from I (always at k = 1).
+      Gate zg;
+      zg.c2 = k > 1 ? fk : nullptr;
+      if ((e = sym<TILE>(R, R, kn, np, R, bk, ck, Z, Qb[qi ^ 1], ak, zg)) != hipSuccess) return e;
+      if (k > 1) {
+        Gate qg;
+        qg.gate = fk;
+        qg.want = 0;
+        if ((e = sym<TILE>(Qb[qi], Z, kn, np, Qb[qi], ak, 1.f, Qb[qi ^ 1], nullptr, 0.f, qg)) != hipSuccess) return e;
+      }
+      qi ^= 1;
+      if (k < steps) {
+        hipLaunchKernelGGL(k_guard_detect<T>, dim3((unsigned)p.batch), dim3(kStageThreads), 0, st, Qb[qi], R,
+                           p.n_pad, p.nn_elems, (int)p.n, a[k], theta, f, kFlagStride, k + 1, status(),
+                           (int32_t)(NS_STATUS_GUARD_RESTART | NS_STATUS_GUARD_STEP(k + 1)));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        Gate rg;
+        rg.gate = f + k + 1;
+        rg.want = 0;
+        T* V = Qb[qi ^ 1];
+        if ((e = sym<TILE>(R, Z, kn, np, R, ak, 1.f, V, nullptr, 0.f, rg)) != hipSuccess) return e;
+        if ((e = sym<TILE>(V, Z, kn, np, V, ak, 1.f, R, nullptr, 0.f, rg)) != hipSuccess) return e;
+      }
+    }
+    return nn_final<TILE>(Qb[qi], 0, false, 0.f, unscale, sel);
+  }
 };
 
 // The kernel builds a call launches, as text (see ns_plan_kernels): one
@@ -615,7 +740,7 @@ const char* form_name(Form f) {
 }
 const char* dtype_name(ns_dtype d) { return d == NS_FP32 ? "f32" : d == NS_FP16 ? "f16" : "bf16"; }
 
-std::string describe_plan(const Plan& p, int steps, uint32_t mask) {
+std::string describe_plan(const Plan& p, int steps, uint32_t mask, bool guard) {
   const int esz = p.esz;
   const int64_t per_k = kRowBytes / esz;
   const int64_t km = round_up(p.m, per_k) / per_k, kn = round_up(p.n, per_k) / per_k;
@@ -644,7 +769,7 @@ std::string describe_plan(const Plan& p, int steps, uint32_t mask) {
     add("out<" + T + "," + IO + "," + E + "," + upd + e_term + ">");
   } else {
     for (int k = 2; k <= steps; ++k)
-      if ((mask >> k) & 1u) add("upd<" + T + "," + T + "," + E + "," + upd + ",noE>");
+      if (guard || ((mask >> k) & 1u)) add("upd<" + T + "," + T + "," + E + "," + upd + ",noE>");
     add("out<" + T + "," + IO + "," + E + "," + upd + ",noE>");
   }
   return out;
@@ -805,6 +930,7 @@ ns_status orthogonalize_impl(void* X, int64_t batch, int64_t rows, int64_t cols,
   ns_status s = make_plan(rows, cols, batch, dtype, mode, opt, &p);
   if (s != NS_OK) return s;
   if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
+  if (opt && !(opt->guard_threshold >= 0.f && isfinite(opt->guard_threshold))) return NS_ERR_INVALID_ARG;
   const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
   if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal, p.io)) != NS_OK) return s;
   if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
@@ -864,6 +990,7 @@ ns_status muon_impl(void* W, const void* G, float* M, int64_t batch, int64_t row
   ns_status s = make_plan(rows, cols, batch, dtype, mode, opt, &p);
   if (s != NS_OK) return s;
   if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
+  if (opt && !(opt->guard_threshold >= 0.f && isfinite(opt->guard_threshold))) return NS_ERR_INVALID_ARG;
   const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
   if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal, p.io)) != NS_OK) return s;
   if (!ws || ws_bytes < muon_total(p) || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return NS_ERR_WORKSPACE;
@@ -963,6 +1090,7 @@ void ns_options_default(ns_options* opt) {
   opt->d_status = nullptr;
   opt->trace = nullptr;
   opt->tile = 0;
+  opt->guard_threshold = 0.f;
 }
 
 size_t ns_workspace_size(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode,
@@ -991,7 +1119,8 @@ int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtyp
                         const ns_options* opt, char* buf, size_t len) {
   Plan p;
   if (make_plan(rows, cols, batch, dtype, mode, opt, &p) != NS_OK || steps < 1 || steps > NS_MAX_STEPS) return -1;
-  const std::string d = describe_plan(p, steps, opt ? opt->restart_mask : (1u << 4));
+  const std::string d =
+      describe_plan(p, steps, opt ? opt->restart_mask : (1u << 4), opt && opt->guard_threshold > 0.f);
   if (buf && len > 0) {
     const size_t n = std::min(len - 1, d.size());
     memcpy(buf, d.data(), n);

@@ -512,7 +512,25 @@ struct SymArgs {
   int batch;         // matrices (read by the persistent kernel)
   float alpha_unused;
   float beta, gamma, delta;
+  // Per-matrix device flags of the guarded Gram iteration (null otherwise),
+  // each read at index bz * flag_stride.  gate: the tile is computed only
+  // when (gate != 0) == gate_want.  c2_gate: C2 is written only when it is
+  // set.  xsel: when set, L and R are taken x_alt elements further on (the
+  // other X buffer).
+  const int32_t* gate;
+  const int32_t* c2_gate;
+  const int32_t* xsel;
+  int64_t x_alt;
+  int32_t gate_want, flag_stride;
 };
+
+// A guarded launch computes matrix bz's tiles only when its flag matches.
+__device__ __forceinline__ bool gated_off(const int32_t* gate, int32_t want, int32_t stride, int bz) {
+  return gate && ((gate[(int64_t)bz * stride] != 0) != (want != 0));
+}
+__device__ __forceinline__ bool flag_set(const int32_t* f, int32_t stride, int bz) {
+  return f && f[(int64_t)bz * stride] != 0;
+}
 
 template <typename T, typename OutT>
 struct NTArgs {
@@ -535,6 +553,13 @@ struct NTArgs {
   float apply_scale;
   int32_t* d_status;    // optional status word: status_bits ORed in on NaN / Inf
   int32_t status_bits;
+  // Guarded Gram iteration (see SymArgs): gate as there; when xsel is set,
+  // X^T is read xt_alt elements further on and Y / Y^T are written y_alt /
+  // yt_alt elements before (the two X buffers swap roles).
+  const int32_t* gate;
+  const int32_t* xsel;
+  int64_t xt_alt, y_alt, yt_alt;
+  int32_t gate_want, flag_stride;
 };
 
 // Ors `bits` into the status word once per wave in which some lane saw a
@@ -853,18 +878,29 @@ __device__ __forceinline__ uint4 with_elem(uint4 v, int k, T d) {
 }
 
 // One upper-triangle tile (tm <= tn) of matrix bz of a symmetric product.
-template <typename T, int TILE, int G>
+// GUARD: the build for the guarded Gram iteration, which reads the device
+// flags of SymArgs; other launches take the build without that code (it
+// changed the schedule of the products enough to cost 6 % of a call).
+template <typename T, int TILE, int G, bool GUARD>
 __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, int bz) {
   using A = Acc<T, TILE, TILE>;
   constexpr int FM = A::FM, FN = A::FN;
   using TL = TileLds<T, TILE, TILE, G>;
   const int64_t ldk_bytes = (int64_t)p.ldk * sizeof(T);
-  const char* Lg = reinterpret_cast<const char*>(p.L + bz * p.sL) + (int64_t)tm * TILE * ldk_bytes;
-  const char* Rg = reinterpret_cast<const char*>(p.R + bz * p.sR) + (int64_t)tn * TILE * ldk_bytes;
+  int64_t xo = 0;
+  if constexpr (GUARD) {
+    if (gated_off(p.gate, p.gate_want, p.flag_stride, bz)) return;
+    xo = flag_set(p.xsel, p.flag_stride, bz) ? p.x_alt : 0;
+  }
+  const char* Lg = reinterpret_cast<const char*>(p.L + bz * p.sL + xo) + (int64_t)tm * TILE * ldk_bytes;
+  const char* Rg = reinterpret_cast<const char*>(p.R + bz * p.sR + xo) + (int64_t)tn * TILE * ldk_bytes;
   constexpr int BK = kRowBytes / sizeof(T);
   const T* E = p.E ? p.E + bz * p.sE : nullptr;
   T* C = p.C + bz * p.sC;
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
+  if constexpr (GUARD) {
+    if (p.c2_gate && !flag_set(p.c2_gate, p.flag_stride, bz)) C2 = nullptr;
+  }
   const bool diag_tile = (tm == tn);
   static_assert(TILE * sizeof(T) <= sizeof(g_c2_diag), "C2 diagonal buffer");
   T* c2d = reinterpret_cast<T*>(g_c2_diag);
@@ -981,19 +1017,19 @@ __device__ __forceinline__ int persistent_piece(int b, int G) { return (b % kXcd
 // GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
 // n x n products into their own kernel symbol, so profiles list them apart.
 // One work-group per upper-triangle tile.
-template <typename T, int TILE, bool GRAM_INPUT, int G = 1>
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool GUARD = false>
 __global__ void __launch_bounds__(kThreads, G) k_sym(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   int tm, tn;
   tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
-  sym_tile<T, TILE, G>(p, tm, tn, blockIdx.y);
+  sym_tile<T, TILE, G, GUARD>(p, tm, tn, blockIdx.y);
 }
 
 // Persistent form: a grid of work-groups looping over the tiles of all
 // matrices in list order, so one tile's stores drain while the next one
 // starts.  A kernel of its own: the loop's live state would push the 256
 // tile past the register file.
-template <typename T, int TILE, bool GRAM_INPUT, int G = 1>
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool GUARD = false>
 __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   const int total = ntri * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
@@ -1001,7 +1037,7 @@ __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
     const int pos = base + piece, bz = pos / ntri;
     int tm, tn;
     tri_tile(pos % ntri, p.tiles, tm, tn);
-    sym_tile<T, TILE, G>(p, tm, tn, bz);
+    sym_tile<T, TILE, G, GUARD>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }
@@ -1009,19 +1045,25 @@ __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
 // Y = alpha E + gamma B (X^T)^T on TM x TN tiles: the update of both forms.
 // CAP: E is taken from the X^T panel in LDS during the main loop; otherwise
 // it is loaded from global memory before the main loop (or absent).
-template <typename T, typename OutT, int TM, int TN, int G, bool CAP>
+template <typename T, typename OutT, int TM, int TN, int G, bool CAP, bool GUARD>
 __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn, int bz) {
   using A = Acc<T, TM, TN>;
   constexpr int FM = A::FM, FN = A::FN;
   using TL = TileLds<OutT, TM, TN, G>;
   const int64_t ldb_bytes = (int64_t)p.ldb * sizeof(T);
   const int64_t ldxt_bytes = (int64_t)p.ldxt * sizeof(T);
+  bool swap = false;
+  if constexpr (GUARD) {
+    if (gated_off(p.gate, p.gate_want, p.flag_stride, bz)) return;
+    swap = flag_set(p.xsel, p.flag_stride, bz);
+  }
   const char* Lg = reinterpret_cast<const char*>(p.B + bz * p.sB) + (int64_t)tm * TM * ldb_bytes;
-  const char* Rg = reinterpret_cast<const char*>(p.XT + bz * p.sXT) + (int64_t)tn * TN * ldxt_bytes;
+  const char* Rg =
+      reinterpret_cast<const char*>(p.XT + bz * p.sXT + (swap ? p.xt_alt : 0)) + (int64_t)tn * TN * ldxt_bytes;
   constexpr int BK = kRowBytes / sizeof(T);
   const T* E = p.E ? p.E + bz * p.sE : nullptr;
-  OutT* Y = p.Y + bz * p.sY;
-  T* YT = p.YT ? p.YT + bz * p.sYT : nullptr;
+  OutT* Y = p.Y + bz * p.sY - (swap ? p.y_alt : 0);
+  T* YT = p.YT ? p.YT + bz * p.sYT - (swap ? p.yt_alt : 0) : nullptr;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
   using EP = EPrefetch<T, TM, TN>;
   EP ep;
@@ -1166,17 +1208,17 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
 // One work-group per tile on a one-dimensional grid over the tiles of all
 // matrices: the list (matrix by matrix, each in grouped_tile order) is cut
 // into one contiguous piece per XCD.
-template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool GUARD = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int pos = xcd_order(blockIdx.x, per * p.batch);
   int tm, tn;
   grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-  nt_tile<T, OutT, TM, TN, G, CAP>(p, tm, tn, pos / per);
+  nt_tile<T, OutT, TM, TN, G, CAP, GUARD>(p, tm, tn, pos / per);
 }
 
 // Persistent form of k_nt (see k_sym_loop).
-template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool GUARD = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int total = per * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
@@ -1184,7 +1226,7 @@ __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
     const int pos = base + piece, bz = pos / per;
     int tm, tn;
     grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-    nt_tile<T, OutT, TM, TN, G, CAP>(p, tm, tn, bz);
+    nt_tile<T, OutT, TM, TN, G, CAP, GUARD>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }

@@ -193,6 +193,78 @@ __global__ void __launch_bounds__(kStageThreads) k_check_finite(const T* p, int6
   report_status(d_status, status_bits, bad);
 }
 
+// ---------------------------------------------------------------------------
+// Guarded Gram iteration: per-matrix device flags, `stride` ints per matrix.
+// Index 0 selects the X buffer (0: the first pair, 1: the second); index k
+// (2 <= k <= steps) is set when a restart happens before step k.
+// ---------------------------------------------------------------------------
+
+// flags[b][0] = 0, flags[b][k] = bit k of the fixed restart mask.
+__global__ void k_guard_init(int32_t* flags, int batch, int stride, uint32_t mask) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < batch * stride) {
+    const int k = i % stride;
+    flags[i] = (k >= 2 && k < 32) ? (int32_t)((mask >> k) & 1u) : 0;
+  }
+}
+
+// After a restart before step k: matrices that restarted now hold their X
+// in the other buffer.
+__global__ void k_guard_flip(int32_t* flags, int batch, int stride, int k) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch && flags[(int64_t)b * stride + k]) flags[(int64_t)b * stride] ^= 1;
+}
+
+// The restart detector, after step k formed Q (one block per matrix).  The
+// accumulated Q has an eigenvalue near the product of the a_j since the
+// last restart in the directions of X's smallest singular values, and
+// stored in fp16 its rounding error grows with that eigenvalue; the largest
+// diagonal entry tracks it.  A restart before step k + 1 is scheduled when
+// max_i |Q_ii| * |a_{k+1}| exceeds theta, or when a diagonal entry of R (a
+// Gram matrix: never negative in exact arithmetic) is negative or not
+// finite (a restart recomputes R from X).  Restarting is then reported through the status
+// word (guard_bits).
+template <typename T>
+__global__ void __launch_bounds__(kStageThreads) k_guard_detect(const T* Q, const T* R, int64_t ld, int64_t nstride,
+                                                               int n_real, float a_next, float theta, int32_t* flags,
+                                                               int stride, int k_next, int32_t* d_status,
+                                                               int32_t guard_bits) {
+  __shared__ float sh_max[kStageThreads / 64];
+  __shared__ int sh_bad[kStageThreads / 64];
+  const int b = blockIdx.x;
+  const T* q = Q + (int64_t)b * nstride;
+  const T* r = R + (int64_t)b * nstride;
+  float m = 0.f;
+  int bad = 0;
+  for (int i = threadIdx.x; i < n_real; i += kStageThreads) {
+    const float qi = to_f32<T>(q[(int64_t)i * (ld + 1)]), ri = to_f32<T>(r[(int64_t)i * (ld + 1)]);
+    if (ri < 0.f || !(fabsf(ri) < __builtin_inff())) bad = 1;
+    m = fmaxf(m, fabsf(qi));  // fmaxf drops a NaN; an Inf schedules a restart
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    m = fmaxf(m, __shfl_down(m, off, 64));
+    bad |= __shfl_down(bad, off, 64);
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    sh_max[w] = m;
+    sh_bad[w] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kStageThreads / 64; ++i) {
+      m = fmaxf(m, sh_max[i]);
+      bad |= sh_bad[i];
+    }
+    int32_t* f = flags + (int64_t)b * stride + k_next;
+    if ((bad || m * fabsf(a_next) > theta) && !*f) {
+      *f = 1;
+      if (d_status) atomicOr(d_status, guard_bits);
+    }
+  }
+}
+
 // Muon momentum: M <- mu M + G (fp32), U = G + mu M (Nesterov) or M, U
 // rounded to IO and stored contiguously (rows x cols per matrix).  One
 // block per row; 8 consecutive elements per thread, vectorized when rows

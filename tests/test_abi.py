@@ -256,6 +256,20 @@ def test_coefficient_range_check_follows_the_scalar_map():
             assert _call(steps=len(sched), abc=sched, mode=mode, ws_bytes=16) == wsp
 
 
+def test_guard_threshold_checks():
+    inv, wsp = 1, 3
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert _call(opt=B.make_options(guard=bad), mode=B.NS_GRAM) == inv
+    assert _call(opt=B.make_options(guard=100.0), mode=B.NS_GRAM, ws_bytes=16) == wsp
+    # The guarded Gram form always enqueues the (gated) restart update.
+    ks = nsa.plan_kernels(300, 700, 1, torch.bfloat16, "gram", restart_mask=0)
+    assert not any(k.startswith("upd<") for k in ks)
+    opt = B.make_options(restart_mask=0, guard=100.0)
+    buf = ctypes.create_string_buffer(512)
+    B.lib().ns_plan_kernels(300, 700, 1, B.NS_BF16, B.NS_GRAM, 5, ctypes.byref(opt), buf, 512)
+    assert "upd<f16,f16,128,tile,noE>" in buf.value.decode().split()
+
+
 def test_plan_kernels_names_the_builds():
     ks = nsa.plan_kernels(4096, 14336, 1, torch.bfloat16, "gram")
     assert ks == ["sumsq<bf16>", "stage<bf16,f16>", "xxt<f16,192,tile>",
