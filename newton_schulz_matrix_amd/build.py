@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libnsortho.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip"]
+SOURCES = ["api.hip"] + [f"kern_{kind}_{t}.hip" for kind in ("sym", "nt")
+                         for t in ("f16_128", "f16_192", "f16_256", "f32_128")]
 
 ARCH = "gfx950"
 

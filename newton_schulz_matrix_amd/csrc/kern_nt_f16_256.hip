@@ -1,0 +1,11 @@
+// kern_nt_f16_256.hip - kernel builds of the updates for one operand type and tile
+// edge (see plan.hpp).
+#define NS_KERNEL_UNIT
+#include "plan.hpp"
+
+namespace nsr {
+
+NS_NT_LAUNCHER(_Float16, _Float16, 256)
+NS_NT_LAUNCHER(_Float16, __bf16, 256)
+
+}  // namespace nsr

@@ -1,0 +1,10 @@
+// kern_sym_f16_192.hip - kernel builds of the symmetric-result products for one operand type and tile
+// edge (see plan.hpp).
+#define NS_KERNEL_UNIT
+#include "plan.hpp"
+
+namespace nsr {
+
+NS_SYM_LAUNCHERS(_Float16, 192)
+
+}  // namespace nsr

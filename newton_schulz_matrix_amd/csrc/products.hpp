@@ -74,9 +74,9 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return
 // The smallest magnitude that rounds to infinity (round to nearest even):
 // a value is finite after rounding to T exactly when its magnitude is below
 // this (NaN compares false).
-template <typename T> constexpr float kRoundsToInf = __builtin_inff();
-template <> constexpr float kRoundsToInf<_Float16> = 65520.0f;            // 65504 + half an ulp
-template <> constexpr float kRoundsToInf<__bf16> = 0x1.ffp127f;          // bf16 max + half an ulp
+template <typename T> inline constexpr float kRoundsToInf = __builtin_inff();
+template <> inline constexpr float kRoundsToInf<_Float16> = 65520.0f;            // 65504 + half an ulp
+template <> inline constexpr float kRoundsToInf<__bf16> = 0x1.ffp127f;          // bf16 max + half an ulp
 
 // Four consecutive elements <-> four floats.
 template <typename T> struct Quad;

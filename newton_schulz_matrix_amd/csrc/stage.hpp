@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(kStageThreads) k_sumsq(const IO* M, int64_t ro
 // scale[b] = prescale / (sqrt(sum of the P partials of matrix b) + eps),
 // summed in a fixed order.  One block per matrix.  A non-finite sum (NaN or
 // Inf in the input) ORs status_bits into the optional status word.
-__global__ void __launch_bounds__(kStageThreads) k_scale(const double* partial, int P, float prescale, float eps,
+static __global__ void __launch_bounds__(kStageThreads) k_scale(const double* partial, int P, float prescale, float eps,
                                                         float* scale, int32_t* d_status, int32_t status_bits) {
   __shared__ double sh[kStageThreads / 64];
   const double* pp = partial + (int64_t)blockIdx.x * P;
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(kStageThreads) k_check_finite(const T* p, int6
 // ---------------------------------------------------------------------------
 
 // flags[b][0] = 0, flags[b][k] = bit k of the fixed restart mask.
-__global__ void k_guard_init(int32_t* flags, int batch, int stride, uint32_t mask) {
+static __global__ void k_guard_init(int32_t* flags, int batch, int stride, uint32_t mask) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < batch * stride) {
     const int k = i % stride;
@@ -210,7 +210,7 @@ __global__ void k_guard_init(int32_t* flags, int batch, int stride, uint32_t mas
 
 // After a restart before step k: matrices that restarted now hold their X
 // in the other buffer.
-__global__ void k_guard_flip(int32_t* flags, int batch, int stride, int k) {
+static __global__ void k_guard_flip(int32_t* flags, int batch, int stride, int k) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < batch && flags[(int64_t)b * stride + k]) flags[(int64_t)b * stride] ^= 1;
 }

@@ -57,7 +57,7 @@ template <> struct KeyOf<float> {
   static __device__ __forceinline__ float value(uint32_t k) { return __uint_as_float(k); }
 };
 
-__global__ void k_select_init(SelectState* st, uint32_t* hist, int nhist, uint64_t rank) {
+static __global__ void k_select_init(SelectState* st, uint32_t* hist, int nhist, uint64_t rank) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nhist) hist[i] = 0u;
   if (i == 0) {
@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(kHistThreads) k_radix_pick(SelectState* st, co
 }
 
 // Explicit lambda: only record it.
-__global__ void k_set_lambda(SelectState* st, float lam, float* d_lambda_out) {
+static __global__ void k_set_lambda(SelectState* st, float lam, float* d_lambda_out) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     st->lambda = lam;
     if (d_lambda_out) *d_lambda_out = lam;
