@@ -10,8 +10,9 @@ products are dense, so the work does not depend on the values.
 
 Other workloads (--workload): the transposed and square Llama shapes, the
 MoE expert batch (128 x 2048 x 1408 and transposed), the NanoGPT-124M
-weight set (three batched calls per step, each on a stream of its own
-unless --serial), the ROOT split of a 2048 x 8192
+weight set (two grouped calls per step -- the square attention weights, and
+the wide and tall MLP weights together -- each on a stream of its own unless
+--serial; --per-shape runs three batched calls), the ROOT split of a 2048 x 8192
 Student-t gradient followed by orthogonalization of its robust part, and a
 256 x 1024 fp32 matrix, and a whole Muon step (momentum, orthogonalization,
 weight update) with the 4096 x 14336 matrix as the gradient.  `value`
@@ -58,6 +59,7 @@ PEAK_HBM_GBS = 8000.0
 # Sources whose change invalidates a committed HBM-traffic measurement.
 KERNEL_SOURCES = ["newton_schulz_matrix_amd/csrc/products.hpp",
                   "newton_schulz_matrix_amd/csrc/stage.hpp",
+                  "newton_schulz_matrix_amd/csrc/plan.hpp",
                   "newton_schulz_matrix_amd/csrc/api.hip"]
 
 
@@ -83,19 +85,22 @@ def parse():
     ap.add_argument("--serial", action="store_true",
                     help="run a multi-call step's calls one after another on "
                          "one stream (default: one stream per call)")
+    ap.add_argument("--per-shape", action="store_true",
+                    help="NanoGPT set: one batched call per stored shape "
+                         "(three calls) instead of two grouped calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-form companion measurement")
     return ap.parse_args()
 
 
-def workload_input(name, shape=None):
+def workload_input(name, shape=None, grouped=True):
     """(list of host input tensors, I/O dtype name, step kind).
 
     The kind is "ns" (orthogonalize each input), "root" (ROOT split, then
     orthogonalize the robust part) or "muon" (a whole Muon step with the
-    input as the gradient).  A 3-D tensor is one batched call; a list of
-    several tensors is run as one call each, in order, per step.
+    input as the gradient).  A 3-D tensor is one batched call, a list of 2-D
+    tensors one grouped call; several inputs run as one call each per step.
     """
     import workloads
     if shape is not None:
@@ -115,6 +120,12 @@ def workload_input(name, shape=None):
     if name == "nanogpt-set":
         import torch
         groups = workloads.nanogpt_set()
+        if grouped:
+            # Two groups: the square attention weights and the MLP weights,
+            # wide and tall together (one shape up to orientation).
+            return ([torch.stack(groups["768x768"]),
+                     list(groups["768x3072"]) + list(groups["3072x768"])],
+                    "bf16", "ns")
         return [torch.stack(g) for g in groups.values()], "bf16", "ns"
     if name == "root-split":
         return [workloads.heavy_tailed()], "bf16", "root"
@@ -190,6 +201,17 @@ def make_step(inputs, mode, args, kind):
     import newton_schulz_matrix_amd as nsa
     calls = []
     for x in inputs:
+        if isinstance(x, list):
+            n, m = min(x[0].shape), max(x[0].shape)
+            ws = torch.empty(nsa.grouped_workspace_size(
+                n, m, len(x), x[0].dtype, mode, args.restart_mask,
+                args.internal, args.tile) + 256, dtype=torch.uint8,
+                device=x[0].device)
+            calls.append((nsa.orthogonalize_grouped, x,
+                          dict(mode=mode, restart_mask=args.restart_mask,
+                               internal=args.internal, workspace=ws,
+                               tile=args.tile), None))
+            continue
         batched = x.dim() == 3
         fn = nsa.orthogonalize_batched if batched else nsa.orthogonalize
         rows, cols = x.shape[-2], x.shape[-1]
@@ -215,7 +237,8 @@ def make_step(inputs, mode, args, kind):
     # Calls on different inputs are independent: with several, each gets a
     # stream of its own (default priority), forked from and joined back into
     # the caller's stream, so one call's short launches overlap another's.
-    streams = ([torch.cuda.Stream(device=inputs[0].device) for _ in calls]
+    dev0 = torch.device("cuda:0")
+    streams = ([torch.cuda.Stream(device=dev0) for _ in calls]
                if len(calls) > 1 and not args.serial else None)
 
     def step(trace=None):
@@ -476,10 +499,17 @@ def main():
     dev = torch.device("cuda:0")
     if args.shape is not None:
         args.workload = f"column-scaled-{args.shape[0]}x{args.shape[1]}"
-    host_inputs, io, kind = workload_input(args.workload, args.shape)
-    inputs = [m.to(dev) for m in host_inputs]
-    shapes = [(m.shape[0] if m.dim() == 3 else 1, m.shape[-2], m.shape[-1])
+    host_inputs, io, kind = workload_input(args.workload, args.shape,
+                                           grouped=not args.per_shape)
+    inputs = [[x.to(dev) for x in m] if isinstance(m, list) else m.to(dev)
               for m in host_inputs]
+    shapes = []
+    for m in host_inputs:
+        if isinstance(m, list):
+            shapes += [(1, x.shape[0], x.shape[1]) for x in m]
+        else:
+            shapes.append((m.shape[0] if m.dim() == 3 else 1, m.shape[-2],
+                           m.shape[-1]))
     matrices = sum(b for b, _, _ in shapes)
     internal = args.internal or ("fp16" if io != "fp32" else "fp32")
     dtype = {"fp16": "f16", "bf16": "bf16", "fp32": "f32"}[internal]
@@ -550,6 +580,8 @@ def main():
                    "restart_mask": args.restart_mask,
                    "tile": args.tile or "auto",
                    "streams": len(inputs) if len(inputs) > 1 and not args.serial else 1,
+                   "calls": len(inputs),
+                   "grouped": any(isinstance(m, list) for m in host_inputs),
                    "parallelism": "single-gpu"},
         "tflops": tflops,
         "mfma_frac": tflops / PEAK_TFLOPS[dtype],
@@ -569,6 +601,7 @@ def main():
         out["quality"] = root_quality(host_inputs[0], args.mode, args)
     if not args.no_cpu_baseline:
         first = host_inputs[0]
+        first = first[0] if isinstance(first, list) else first
         sample = first if first.dim() == 2 else first[0]
         cb = cpu_baseline(sample, args.mode, args.restart_mask)
         if first.dim() == 3 or len(host_inputs) > 1:

@@ -222,6 +222,48 @@ ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows,
                                    ns_stream_t stream);
 
 /*
+ * Grouped call: `count` matrices that share one shape up to orientation,
+ * each with its own storage, every stage launched once for all of them (the
+ * Gram-NS essay on showapi.com, sections 2.3 and 4.1: experts launched
+ * together and advancing in step).  With n <= m the oriented shape, member i
+ * is the matrix at members[i].data (device memory), n x m with leading
+ * dimension ld when transposed == 0, or m x n (stored transposed, like a
+ * tall weight) with leading dimension ld when transposed == 1; it is
+ * orthogonalized in place in its own layout.  So the 768 x 3072 and
+ * 3072 x 768 matrices of a transformer's MLP go in one group.
+ *
+ *   members  host array of `count` entries, written into the workspace on
+ *            the stream by the call (through kernel arguments, no host
+ *            copy or synchronization), so it may be reused once the call
+ *            returns; data not NULL,
+ *            transposed 0 or 1, reserved 0, ld >= m (transposed == 0) or
+ *            >= n (transposed == 1), else NS_ERR_INVALID_ARG.
+ *   count    1..65535 and n, m as for ns_orthogonalize_batched's shape.
+ *   workspace   ns_grouped_workspace_size(n, m, count, ...) bytes.
+ * Every member's result equals ns_orthogonalize's on that matrix bit for
+ * bit.  Members must not overlap.  Other arguments and errors as for
+ * ns_orthogonalize_batched.
+ */
+typedef struct ns_matrix {
+  void* data;
+  int64_t ld;
+  int32_t transposed;
+  int32_t reserved;
+} ns_matrix;
+
+size_t ns_grouped_workspace_size(int64_t n, int64_t m, int64_t count,
+                                 ns_dtype dtype, ns_mode mode,
+                                 const ns_options* opt);
+
+ns_status ns_orthogonalize_grouped(const ns_matrix* members, int64_t count,
+                                   int64_t n, int64_t m, ns_dtype dtype,
+                                   int32_t steps, const float* a,
+                                   const float* b, const float* c,
+                                   ns_mode mode, const ns_options* opt,
+                                   void* workspace, size_t workspace_bytes,
+                                   ns_stream_t stream);
+
+/*
  * ns_orthogonalize_batched without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, serving loops
  * and harnesses that forbid hipMalloc).  It calls no allocating routine: its

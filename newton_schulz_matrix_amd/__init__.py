@@ -12,7 +12,8 @@ library does all the work; this package only marshals arguments.
 from .flops import gram_flops, ns_flops, standard_flops
 from ._binding import (NS_MAX_STEPS, TUNED_ABC, NSError, lib, muon_step,
                        muon_workspace_size, orthogonalize,
-                       orthogonalize_batched, plan_kernels,
+                       orthogonalize_batched, orthogonalize_grouped,
+                       grouped_workspace_size, plan_kernels,
                        soft_threshold_split, status_code, status_string,
                        workspace_size)
 from .coeffs import fit_coefficients, root_coefficients
@@ -20,7 +21,8 @@ from .coeffs import fit_coefficients, root_coefficients
 __all__ = [
     "NS_MAX_STEPS", "TUNED_ABC", "NSError", "lib", "muon_step",
     "muon_workspace_size", "orthogonalize",
-    "orthogonalize_batched", "plan_kernels", "soft_threshold_split",
+    "orthogonalize_batched", "orthogonalize_grouped",
+    "grouped_workspace_size", "plan_kernels", "soft_threshold_split",
     "status_code", "status_string",
     "workspace_size", "gram_flops", "ns_flops", "standard_flops",
     "fit_coefficients", "root_coefficients",

@@ -70,6 +70,14 @@ class Options(ctypes.Structure):
                 ("guard_threshold", ctypes.c_float)]
 
 
+class Matrix(ctypes.Structure):
+    """ns_matrix: one member of a grouped call."""
+    _fields_ = [("data", ctypes.c_void_p),
+                ("ld", ctypes.c_int64),
+                ("transposed", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 KERNEL_KINDS = ("norm", "stage", "gram", "sym", "update", "threshold",
                 "momentum")
 
@@ -129,6 +137,20 @@ _SIGNATURES = {
                       ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                       ctypes.POINTER(Options), ctypes.c_void_p,
                       ctypes.c_size_t, ctypes.c_void_p]),
+    "ns_grouped_workspace_size": (ctypes.c_size_t,
+                                  [ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(Options)]),
+    "ns_orthogonalize_grouped": (ctypes.c_int,
+                                 [ctypes.POINTER(Matrix), ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int, ctypes.c_int32,
+                                  ctypes.POINTER(ctypes.c_float),
+                                  ctypes.POINTER(ctypes.c_float),
+                                  ctypes.POINTER(ctypes.c_float),
+                                  ctypes.c_int, ctypes.POINTER(Options),
+                                  ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]),
     "ns_static_scratch_bytes": (ctypes.c_size_t, []),
     "ns_orthogonalize_static": (ctypes.c_int,
                                 [ctypes.c_void_p, ctypes.c_int64,
@@ -341,6 +363,62 @@ def orthogonalize_batched(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,
         ctypes.c_void_p(wptr), wbytes, _stream_handle(x.device))
     _check(st, "ns_orthogonalize_batched")
     return x
+
+
+def orthogonalize_grouped(mats: Sequence[torch.Tensor], steps: int = 5,
+                          abc=TUNED_ABC, mode: str = "gram",
+                          restart_mask: int = 1 << 4, eps: float = 1e-7,
+                          internal: Optional[str] = None,
+                          status: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          trace: Optional[Trace] = None, tile: int = 0,
+                          guard: float = 0.0) -> Sequence[torch.Tensor]:
+    """Orthogonalize 2-D device matrices of one shape up to orientation (for
+    example 768 x 3072 and 3072 x 768) in place, each stage launched once
+    for all of them; returns ``mats``."""
+    if not mats:
+        raise ValueError("expects at least one matrix")
+    dtype, device = mats[0].dtype, mats[0].device
+    shapes = {(min(x.shape), max(x.shape)) for x in mats}
+    if len(shapes) != 1:
+        raise ValueError("all matrices must have one shape up to orientation")
+    n, m = shapes.pop()
+    table = (Matrix * len(mats))()
+    for i, x in enumerate(mats):
+        _check_matrix(x, 2)
+        if x.dtype != dtype or x.device != device:
+            raise ValueError("all matrices must share dtype and device")
+        rows, cols = x.shape
+        table[i].data = x.data_ptr()
+        table[i].ld = x.stride(0) if rows > 1 else cols
+        table[i].transposed = 1 if rows > cols else 0
+        table[i].reserved = 0
+    code = dtype_code(dtype)
+    opt = make_options(restart_mask, eps, internal, status, trace, tile, guard)
+    need = int(lib().ns_grouped_workspace_size(n, m, len(mats), code,
+                                               _MODE_CODE[mode],
+                                               ctypes.byref(opt)))
+    if need == 0:
+        raise NSError(1, "ns_grouped_workspace_size")
+    wptr, wbytes, keep = _workspace(need, device, workspace)
+    a, b, c = _coefficients(abc, steps)
+    st = lib().ns_orthogonalize_grouped(
+        table, len(mats), n, m, code, steps, a, b, c, _MODE_CODE[mode],
+        ctypes.byref(opt), ctypes.c_void_p(wptr), wbytes,
+        _stream_handle(device))
+    _check(st, "ns_orthogonalize_grouped")
+    return mats
+
+
+def grouped_workspace_size(n: int, m: int, count: int,
+                           dtype: torch.dtype = torch.bfloat16,
+                           mode: str = "gram", restart_mask: int = 1 << 4,
+                           internal: Optional[str] = None,
+                           tile: int = 0) -> int:
+    opt = make_options(restart_mask, 1e-7, internal, tile=tile)
+    return int(lib().ns_grouped_workspace_size(n, m, count, dtype_code(dtype),
+                                               _MODE_CODE[mode],
+                                               ctypes.byref(opt)))
 
 
 def orthogonalize_static(x: torch.Tensor, steps: int = 5, abc=TUNED_ABC,

@@ -325,6 +325,65 @@ int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtyp
   return (int64_t)d.size() + 1;
 }
 
+// A grouped call's member table reaches the device through kernel
+// arguments, up to kTableChunk entries per launch (3 KiB of arguments), so
+// the call needs neither a copy from pageable host memory (which can make
+// the host wait for the stream) nor a host synchronization.
+constexpr int kTableChunk = 128;
+struct TableChunk {
+  ns_matrix m[kTableChunk];
+  int32_t count;
+};
+
+static __global__ void k_write_table(TableChunk c, ns_matrix* dst) {
+  const int i = threadIdx.x;
+  if (i < c.count) dst[i] = c.m[i];
+}
+
+// Grouped call: the workspace of a batch of `count` n x m matrices, then the
+// members' table.
+size_t grouped_table_offset(const Plan& p) { return align_up(p.total); }
+size_t grouped_total(const Plan& p) { return grouped_table_offset(p) + align_up((size_t)p.batch * sizeof(ns_matrix)); }
+
+size_t ns_grouped_workspace_size(int64_t n, int64_t m, int64_t count, ns_dtype dtype, ns_mode mode,
+                                 const ns_options* opt) {
+  Plan p;
+  if (n > m || make_plan(n, m, count, dtype, mode, opt, &p) != NS_OK) return 0;
+  return grouped_total(p);
+}
+
+ns_status ns_orthogonalize_grouped(const ns_matrix* members, int64_t count, int64_t n, int64_t m, ns_dtype dtype,
+                                   int32_t steps, const float* a, const float* b, const float* c, ns_mode mode,
+                                   const ns_options* opt, void* workspace, size_t workspace_bytes,
+                                   ns_stream_t stream) {
+  if (!members || n < 1 || n > m) return NS_ERR_INVALID_ARG;
+  Plan p;
+  ns_status s = make_plan(n, m, count, dtype, mode, opt, &p);
+  if (s != NS_OK) return s;
+  for (int64_t i = 0; i < count; ++i) {
+    const ns_matrix& mb = members[i];
+    if (!mb.data || (mb.transposed != 0 && mb.transposed != 1) || mb.reserved != 0) return NS_ERR_INVALID_ARG;
+    if (mb.ld < (mb.transposed ? n : m)) return NS_ERR_INVALID_ARG;
+  }
+  if (opt && !(opt->eps >= 0.f && isfinite(opt->eps))) return NS_ERR_INVALID_ARG;
+  if (opt && !(opt->guard_threshold >= 0.f && isfinite(opt->guard_threshold))) return NS_ERR_INVALID_ARG;
+  const uint32_t mask = opt ? opt->restart_mask : (1u << 4);
+  if ((s = check_coefficients(steps, a, b, c, mode, mask, p.internal, p.io)) != NS_OK) return s;
+  if (!workspace || workspace_bytes < grouped_total(p) || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return NS_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  ns_matrix* table = reinterpret_cast<ns_matrix*>(reinterpret_cast<char*>(workspace) + grouped_table_offset(p));
+  for (int64_t i0 = 0; i0 < count; i0 += kTableChunk) {
+    TableChunk chunk;
+    chunk.count = (int32_t)std::min<int64_t>(kTableChunk, count - i0);
+    memcpy(chunk.m, members + i0, (size_t)chunk.count * sizeof(ns_matrix));
+    hipLaunchKernelGGL(k_write_table, dim3(1), dim3(kTableChunk), 0, st, chunk, table + i0);
+    if (hipGetLastError() != hipSuccess) return NS_ERR_HIP;
+  }
+  IoSpec io{nullptr, m, 0, nullptr, m, 0, false, 0.f, table};
+  return dispatch_types(p, OrthCall{p, io, steps, a, b, c, opt, workspace, st});
+}
+
 size_t ns_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 ns_status ns_orthogonalize_static(void* X, int64_t batch, int64_t rows, int64_t cols, int64_t ld, int64_t batch_stride,

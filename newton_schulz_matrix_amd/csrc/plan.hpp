@@ -301,7 +301,7 @@ inline Form nt_form(int edge, int esz, int64_t tiles, int64_t ktiles) {
   return Form::kTile;
 }
 
-template <typename T, int TILE, bool GRAM_INPUT, bool GUARD>
+template <typename T, int TILE, bool GRAM_INPUT, bool EXT>
 hipError_t launch_sym_g(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
   const int64_t ntri = (int64_t)a.tiles * (a.tiles + 1) / 2;
   const int ktiles = a.K / (kRowBytes / (int)sizeof(T));
@@ -310,20 +310,20 @@ hipError_t launch_sym_g(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents
   switch (sym_form(TILE, (int)sizeof(T), ntri * batch, ktiles)) {
     case Form::kPairLoop:
       if constexpr (kHasPairKernels<T, TILE>)
-        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2, GUARD>, dim3(2 * kPersistentGroups), dim3(kThreads), s,
+        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2, EXT>, dim3(2 * kPersistentGroups), dim3(kThreads), s,
                              ev, a);
       break;
     case Form::kPairTile:
       if constexpr (kHasPairKernels<T, TILE>)
-        return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2, GUARD>, tiles_grid, dim3(kThreads), s, ev, a);
+        return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2, EXT>, tiles_grid, dim3(kThreads), s, ev, a);
       break;
     case Form::kLoop:
       if constexpr (TILE <= 192)
-        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 1, GUARD>, dim3(kPersistentGroups), dim3(kThreads), s, ev,
+        return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 1, EXT>, dim3(kPersistentGroups), dim3(kThreads), s, ev,
                              a);
       break;
     case Form::kTile:
-      return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 1, GUARD>, tiles_grid, dim3(kThreads), s, ev, a);
+      return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 1, EXT>, tiles_grid, dim3(kThreads), s, ev, a);
   }
   return hipErrorInvalidConfiguration;
 }
@@ -336,7 +336,7 @@ hipError_t launch_sym(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents e
   return launch_sym_g<T, TILE, GRAM_INPUT, false>(a, batch, s, ev);
 }
 
-template <typename T, typename OutT, int TILE, bool CAP, bool GUARD>
+template <typename T, typename OutT, int TILE, bool CAP, bool EXT>
 hipError_t launch_nt_g(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
   constexpr int TN = nn_tile_n(TILE);
   const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
@@ -345,15 +345,15 @@ hipError_t launch_nt_g(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEv
   switch (nt_form(TILE, (int)sizeof(T), per * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
     case Form::kPairTile:
       if constexpr (kHasPairKernels<T, TILE>)
-        return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP, GUARD>, flat, dim3(kThreads), s, ev, a);
+        return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP, EXT>, flat, dim3(kThreads), s, ev, a);
       break;
     case Form::kLoop:
       if constexpr (TILE <= 192)
-        return launch_kernel(k_nt_loop<T, OutT, TILE, TN, 1, CAP, GUARD>, dim3(kPersistentGroups), dim3(kThreads), s,
+        return launch_kernel(k_nt_loop<T, OutT, TILE, TN, 1, CAP, EXT>, dim3(kPersistentGroups), dim3(kThreads), s,
                              ev, a);
       break;
     case Form::kTile:
-      return launch_kernel(k_nt<T, OutT, TILE, TN, 1, CAP, GUARD>, flat, dim3(kThreads), s, ev, a);
+      return launch_kernel(k_nt<T, OutT, TILE, TN, 1, CAP, EXT>, flat, dim3(kThreads), s, ev, a);
     case Form::kPairLoop:
       break;
   }
@@ -370,12 +370,16 @@ hipError_t launch_nt_cap(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, Launch
 // Gram form) and the other tiles take the kernels without the capture.
 template <typename T, typename OutT, int TILE>
 hipError_t launch_nt(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEvents ev) {
-  // The guarded Gram iteration's updates have no E term.
-  if (a.gate || a.xsel) return a.E ? hipErrorInvalidValue : launch_nt_g<T, OutT, TILE, false, true>(a, batch, s, ev);
+  // Launches with extended arguments (guard flags, a grouped call's member
+  // table) take the kernels built to read them.
+  const bool ext = a.gate || a.xsel || a.members;
   if constexpr (EPrefetch<T, TILE, nn_tile_n(TILE)>::kEnabled) {
-    if (a.E) return launch_nt_cap<T, OutT, TILE, true>(a, batch, s, ev);
+    if (a.E)
+      return ext ? launch_nt_g<T, OutT, TILE, true, true>(a, batch, s, ev)
+                 : launch_nt_cap<T, OutT, TILE, true>(a, batch, s, ev);
   }
-  return launch_nt_cap<T, OutT, TILE, false>(a, batch, s, ev);
+  return ext ? launch_nt_g<T, OutT, TILE, false, true>(a, batch, s, ev)
+             : launch_nt_cap<T, OutT, TILE, false>(a, batch, s, ev);
 }
 
 // Device flags a launch of the guarded Gram iteration reads (see SymArgs):
@@ -398,6 +402,7 @@ struct Runner {
   int64_t ld, bstride;
   IO* out;                   // written by the final epilogue
   int64_t out_ld, out_bstride;
+  const ns_matrix* members;  // grouped call: the members' layouts (device), else null
   bool accumulate;           // false: out = result; true: out += apply * result
   float apply;
   const ns_options* opt;
@@ -419,7 +424,7 @@ struct Runner {
   hipError_t sym(const T* L, const T* R, int K, int ldk, const T* E, float beta, float gamma, T* C, T* C2,
                  float delta, const Gate& g = Gate{}) const {
     if (E && E != L) return hipErrorInvalidValue;
-    SymArgs<T> a;
+    SymArgs<T> a{};
     a.L = L;
     a.R = R;
     a.E = E;
@@ -479,7 +484,7 @@ struct Runner {
   // is 0).
   template <int TILE>
   hipError_t nn_internal(const T* B, int xin, bool with_e, float alpha, int xout, const Gate& g = Gate{}) const {
-    NTArgs<T, T> a;
+    NTArgs<T, T> a{};
     a.B = B;
     a.XT = xtbuf(xin);
     a.E = with_e ? xbuf(xin) : nullptr;
@@ -525,7 +530,7 @@ struct Runner {
   // The caller's matrix = out_scale * (alpha * X_in + B X_in), oriented back.
   template <int TILE>
   hipError_t nn_final(const T* B, int xin, bool with_e, float alpha, float out_scale, const Gate& g = Gate{}) const {
-    NTArgs<T, IO> a;
+    NTArgs<T, IO> a{};
     a.B = B;
     a.XT = xtbuf(xin);
     a.E = with_e ? xbuf(xin) : nullptr;
@@ -562,6 +567,7 @@ struct Runner {
     a.y_alt = 0;
     a.yt_alt = 0;
     a.flag_stride = kFlagStride;
+    a.members = members;
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (1.0 + (with_e ? 1.0 : 0.0)) + n * m * sizeof(IO));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
@@ -576,7 +582,8 @@ struct Runner {
     const double elems = (double)p.rows * (double)p.cols * (double)p.batch;
     hipError_t e = tr.run(NS_KERNEL_NORM, 0.0, elems * sizeof(IO), [&](LaunchEvents ev) {
       return launch_kernel((k_sumsq<IO>), dim3(p.partials, (unsigned)p.batch), dim3(kStageThreads), st, ev,
-                           (const IO*)user, p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, partial, p.partials);
+                           (const IO*)user, p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, partial, p.partials,
+                           members);
     });
     if (e != hipSuccess) return e;
     float* scales = reinterpret_cast<float*>(ws + p.off_scale);
@@ -587,7 +594,7 @@ struct Runner {
       const int bi = (int)(p.n_pad / 64), bj = (int)(p.m_pad / 64);
       return launch_kernel(k_stage_pair<IO, T>, dim3((unsigned)(bi * bj), (unsigned)p.batch), dim3(kStageThreads), st,
                            ev, (const IO*)user, p.rows, p.cols, ld, bstride, vec_ok ? 1 : 0, (const float*)scales,
-                           xbuf(0), xtbuf(0), p.n_pad, p.m_pad, p.x_elems, p.transposed ? 1 : 0, bj);
+                           xbuf(0), xtbuf(0), p.n_pad, p.m_pad, p.x_elems, p.transposed ? 1 : 0, bj, members);
     });
   }
 
@@ -786,6 +793,7 @@ struct IoSpec {
   int64_t out_ld, out_bstride;
   bool accumulate;  // false: out = result; true: out += apply * result
   float apply;
+  const ns_matrix* members = nullptr;  // grouped call (device table), else null
 };
 
 template <typename T, typename IO>
@@ -800,6 +808,7 @@ ns_status run_typed(const Plan& p, const IoSpec& io, int steps, const float* a, 
                   reinterpret_cast<IO*>(io.out),
                   io.out_ld,
                   io.out_bstride,
+                  io.members,
                   io.accumulate,
                   io.apply,
                   opt,

@@ -42,6 +42,8 @@
 
 #include <type_traits>
 
+#include "../../include/nsortho.h"
+
 namespace nsk {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -560,6 +562,10 @@ struct NTArgs {
   const int32_t* xsel;
   int64_t xt_alt, y_alt, yt_alt;
   int32_t gate_want, flag_stride;
+  // Grouped call (final output only): matrix bz of the batch is written to
+  // members[bz].data with leading dimension members[bz].ld, transposed when
+  // members[bz].transposed; Y, sY, ldy and transpose_out are then unused.
+  const ns_matrix* members;
 };
 
 // Ors `bits` into the status word once per wave in which some lane saw a
@@ -878,17 +884,18 @@ __device__ __forceinline__ uint4 with_elem(uint4 v, int k, T d) {
 }
 
 // One upper-triangle tile (tm <= tn) of matrix bz of a symmetric product.
-// GUARD: the build for the guarded Gram iteration, which reads the device
-// flags of SymArgs; other launches take the build without that code (it
-// changed the schedule of the products enough to cost 6 % of a call).
-template <typename T, int TILE, int G, bool GUARD>
+// EXT: the build that reads the extended arguments (the guarded Gram
+// iteration's device flags; for updates also the member table of a grouped
+// call); other launches take the build without that code (it changed the
+// schedule of the products enough to cost 6 % of a call).
+template <typename T, int TILE, int G, bool EXT>
 __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, int bz) {
   using A = Acc<T, TILE, TILE>;
   constexpr int FM = A::FM, FN = A::FN;
   using TL = TileLds<T, TILE, TILE, G>;
   const int64_t ldk_bytes = (int64_t)p.ldk * sizeof(T);
   int64_t xo = 0;
-  if constexpr (GUARD) {
+  if constexpr (EXT) {
     if (gated_off(p.gate, p.gate_want, p.flag_stride, bz)) return;
     xo = flag_set(p.xsel, p.flag_stride, bz) ? p.x_alt : 0;
   }
@@ -898,7 +905,7 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
   const T* E = p.E ? p.E + bz * p.sE : nullptr;
   T* C = p.C + bz * p.sC;
   T* C2 = p.C2 ? p.C2 + bz * p.sC2 : nullptr;
-  if constexpr (GUARD) {
+  if constexpr (EXT) {
     if (p.c2_gate && !flag_set(p.c2_gate, p.flag_stride, bz)) C2 = nullptr;
   }
   const bool diag_tile = (tm == tn);
@@ -1017,19 +1024,19 @@ __device__ __forceinline__ int persistent_piece(int b, int G) { return (b % kXcd
 // GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
 // n x n products into their own kernel symbol, so profiles list them apart.
 // One work-group per upper-triangle tile.
-template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool GUARD = false>
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool EXT = false>
 __global__ void __launch_bounds__(kThreads, G) k_sym(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   int tm, tn;
   tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
-  sym_tile<T, TILE, G, GUARD>(p, tm, tn, blockIdx.y);
+  sym_tile<T, TILE, G, EXT>(p, tm, tn, blockIdx.y);
 }
 
 // Persistent form: a grid of work-groups looping over the tiles of all
 // matrices in list order, so one tile's stores drain while the next one
 // starts.  A kernel of its own: the loop's live state would push the 256
 // tile past the register file.
-template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool GUARD = false>
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool EXT = false>
 __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   const int total = ntri * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
@@ -1037,7 +1044,7 @@ __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
     const int pos = base + piece, bz = pos / ntri;
     int tm, tn;
     tri_tile(pos % ntri, p.tiles, tm, tn);
-    sym_tile<T, TILE, G, GUARD>(p, tm, tn, bz);
+    sym_tile<T, TILE, G, EXT>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }
@@ -1045,7 +1052,7 @@ __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
 // Y = alpha E + gamma B (X^T)^T on TM x TN tiles: the update of both forms.
 // CAP: E is taken from the X^T panel in LDS during the main loop; otherwise
 // it is loaded from global memory before the main loop (or absent).
-template <typename T, typename OutT, int TM, int TN, int G, bool CAP, bool GUARD>
+template <typename T, typename OutT, int TM, int TN, int G, bool CAP, bool EXT>
 __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn, int bz) {
   using A = Acc<T, TM, TN>;
   constexpr int FM = A::FM, FN = A::FN;
@@ -1053,7 +1060,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   const int64_t ldb_bytes = (int64_t)p.ldb * sizeof(T);
   const int64_t ldxt_bytes = (int64_t)p.ldxt * sizeof(T);
   bool swap = false;
-  if constexpr (GUARD) {
+  if constexpr (EXT) {
     if (gated_off(p.gate, p.gate_want, p.flag_stride, bz)) return;
     swap = flag_set(p.xsel, p.flag_stride, bz);
   }
@@ -1064,6 +1071,16 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   const T* E = p.E ? p.E + bz * p.sE : nullptr;
   OutT* Y = p.Y + bz * p.sY - (swap ? p.y_alt : 0);
   T* YT = p.YT ? p.YT + bz * p.sYT - (swap ? p.yt_alt : 0) : nullptr;
+  int64_t ldy = p.ldy;
+  int transpose_out = p.transpose_out;
+  if constexpr (EXT) {
+    if (p.members) {
+      const ns_matrix mb = p.members[bz];
+      Y = reinterpret_cast<OutT*>(mb.data);
+      ldy = mb.ld;
+      transpose_out = mb.transposed;
+    }
+  }
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
   using EP = EPrefetch<T, TM, TN>;
   EP ep;
@@ -1140,7 +1157,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
     for (int it = 0; it < kChunks / kThreads; ++it) {
       const int q = it * kThreads + threadIdx.x;
       const int r = q / TL::kCPR, c = q % TL::kCPR;
-      *reinterpret_cast<uint4*>(Y + (row0 + r) * p.ldy + col0 + c * kEC) =
+      *reinterpret_cast<uint4*>(Y + (row0 + r) * ldy + col0 + c * kEC) =
           *reinterpret_cast<const uint4*>(TL::chunk(r, c));
     }
     if (YT) {
@@ -1157,9 +1174,9 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
         }
       }
     }
-  } else if (!p.transpose_out) {
+  } else if (!transpose_out) {
     // Caller's matrix, same orientation: rows i < n_real, columns j < m_real.
-    const bool vec = (p.ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    const bool vec = (ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
 #pragma unroll 6
     for (int it = 0; it < kChunks / kThreads; ++it) {
       const int q = it * kThreads + threadIdx.x;
@@ -1167,7 +1184,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
       const int64_t i = row0 + r, j0 = col0 + c * kEC;
       if (i >= p.n_real || j0 >= p.m_real) continue;
       const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
-      OutT* dst = Y + i * p.ldy + j0;
+      OutT* dst = Y + i * ldy + j0;
       if (vec && j0 + kEC <= p.m_real) {
         final_chunk(dst, val, p.accumulate, p.apply_scale);
       } else {
@@ -1178,7 +1195,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   } else {
     // Caller's matrix is the transpose: its row j holds tile column j, in
     // TM / kEC chunks of kEC tile rows.
-    const bool vec = (p.ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    const bool vec = (ldy % kEC) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
 #pragma unroll 1
     for (int it = 0; it < kBIters; ++it) {
       const int q = it * kThreads + threadIdx.x;
@@ -1192,7 +1209,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
       for (int e = 0; e < kEC; ++e) {
         const int64_t j = col0 + cb * kEC + e;
         if (j >= p.m_real) continue;
-        OutT* dst = Y + j * p.ldy + i0;
+        OutT* dst = Y + j * ldy + i0;
         if (vec && i0 + kEC <= p.n_real) {
           final_chunk(dst, cols[e], p.accumulate, p.apply_scale);
         } else {
@@ -1208,17 +1225,17 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
 // One work-group per tile on a one-dimensional grid over the tiles of all
 // matrices: the list (matrix by matrix, each in grouped_tile order) is cut
 // into one contiguous piece per XCD.
-template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool GUARD = false>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool EXT = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int pos = xcd_order(blockIdx.x, per * p.batch);
   int tm, tn;
   grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-  nt_tile<T, OutT, TM, TN, G, CAP, GUARD>(p, tm, tn, pos / per);
+  nt_tile<T, OutT, TM, TN, G, CAP, EXT>(p, tm, tn, pos / per);
 }
 
 // Persistent form of k_nt (see k_sym_loop).
-template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool GUARD = false>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool EXT = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int total = per * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
@@ -1226,7 +1243,7 @@ __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
     const int pos = base + piece, bz = pos / per;
     int tm, tn;
     grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-    nt_tile<T, OutT, TM, TN, G, CAP, GUARD>(p, tm, tn, bz);
+    nt_tile<T, OutT, TM, TN, G, CAP, EXT>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }

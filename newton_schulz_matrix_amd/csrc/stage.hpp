@@ -37,11 +37,36 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
 // partial[b * P + blockIdx.x] = sum of squares over rows blockIdx.x,
 // blockIdx.x + P, ... of matrix b (accumulated in fp64).  The vector path
 // keeps four independent 16-byte loads in flight per thread.
+// A grouped call's member b (members not null) replaces the batch layout: it
+// starts at members[b].data with leading dimension members[b].ld and holds
+// the rows x cols matrix transposed when members[b].transposed; 16-byte
+// loads where its rows allow them.
+template <typename IO>
+__device__ __forceinline__ void member_layout(const ns_matrix* members, int b, const IO*& A, int64_t& rows,
+                                              int64_t& cols, int64_t& ld, int& vec_ok, int& transposed) {
+  const ns_matrix mb = members[b];
+  A = reinterpret_cast<const IO*>(mb.data);
+  ld = mb.ld;
+  transposed = mb.transposed;
+  if (transposed) {
+    const int64_t t = rows;
+    rows = cols;
+    cols = t;
+  }
+  constexpr int V = 16 / sizeof(IO);
+  vec_ok = cols % V == 0 && ld % V == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+}
+
 template <typename IO>
 __global__ void __launch_bounds__(kStageThreads) k_sumsq(const IO* M, int64_t rows, int64_t cols, int64_t ld,
-                                                        int64_t bstride, int vec_ok, double* partial, int P) {
+                                                        int64_t bstride, int vec_ok, double* partial, int P,
+                                                        const ns_matrix* members) {
   __shared__ double sh[kStageThreads / 64];
   const IO* A = M + (int64_t)blockIdx.y * bstride;
+  if (members) {
+    int transposed;
+    member_layout(members, blockIdx.y, A, rows, cols, ld, vec_ok, transposed);
+  }
   double s0 = 0.0, s1 = 0.0;
   constexpr int V = 16 / sizeof(IO);
   if (vec_ok) {
@@ -115,16 +140,18 @@ template <typename IO, typename T>
 __global__ void __launch_bounds__(kStageThreads) k_stage_pair(const IO* M, int64_t rows, int64_t cols, int64_t ld,
                                                              int64_t bstride, int vec_ok, const float* scales, T* X,
                                                              T* XT, int64_t n_pad, int64_t m_pad, int64_t xstride,
-                                                             int transposed, int blocks_j) {
+                                                             int transposed, int blocks_j,
+                                                             const ns_matrix* members) {
   constexpr int kB = 64, kV = 8;
   __shared__ float tile[kB][kB + 1];
   const int b = blockIdx.y;
   const float scale = scales[b];
+  const IO* src = M + (int64_t)b * bstride;
+  if (members) member_layout(members, b, src, rows, cols, ld, vec_ok, transposed);
   const int64_t i0 = (int64_t)(blockIdx.x / blocks_j) * kB;  // X rows
   const int64_t j0 = (int64_t)(blockIdx.x % blocks_j) * kB;  // X columns
   // The caller's block: rows r0.., columns c0.. of M.
   const int64_t r0 = transposed ? j0 : i0, c0 = transposed ? i0 : j0;
-  const IO* src = M + (int64_t)b * bstride;
   for (int q = threadIdx.x; q < kB * (kB / kV); q += kStageThreads) {
     const int r = q / (kB / kV), c = (q % (kB / kV)) * kV;
     const int64_t mr = r0 + r, mc = c0 + c;

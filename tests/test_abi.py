@@ -256,6 +256,34 @@ def test_coefficient_range_check_follows_the_scalar_map():
             assert _call(steps=len(sched), abc=sched, mode=mode, ws_bytes=16) == wsp
 
 
+def test_grouped_argument_checks():
+    lib = B.lib()
+    a, b, c = B._coefficients(B.TUNED_ABC, 5)
+    # The workspace is the batch's plus the member table.
+    plain = nsa.workspace_size(300, 700, 24, torch.bfloat16, "gram")
+    grouped = nsa.grouped_workspace_size(300, 700, 24, torch.bfloat16, "gram")
+    assert plain + 24 * 24 <= grouped <= plain + 24 * 24 + 512
+    assert nsa.grouped_workspace_size(700, 300, 24) == 0      # n > m
+    need = grouped
+
+    def call(members, n=300, m=700, wsb=None):
+        arr = (B.Matrix * len(members))()
+        for i, (data, ld, tr, res) in enumerate(members):
+            arr[i].data, arr[i].ld, arr[i].transposed, arr[i].reserved = data, ld, tr, res
+        return lib.ns_orthogonalize_grouped(arr, len(members), n, m, B.NS_BF16, 5, a, b, c, B.NS_GRAM, None,
+                                            ctypes.c_void_p(256), need if wsb is None else wsb, None)
+    ok = (256, 700, 0, 0)
+    assert call([ok, (512, 300, 1, 0)], wsb=16) == 3          # arguments fine; workspace too small
+    assert call([ok, (0, 700, 0, 0)]) == 1                     # null member
+    assert call([ok, (256, 699, 0, 0)]) == 1                   # ld below the stored width
+    assert call([ok, (256, 299, 1, 0)]) == 1
+    assert call([ok, (256, 700, 2, 0)]) == 1                   # transposed not 0 or 1
+    assert call([ok, (256, 700, 0, 5)]) == 1                   # reserved not 0
+    assert call([ok], n=701, m=700) == 1                       # n > m
+    assert lib.ns_orthogonalize_grouped(None, 1, 300, 700, B.NS_BF16, 5, a, b, c, B.NS_GRAM, None,
+                                        ctypes.c_void_p(256), need, None) == 1
+
+
 def test_guard_threshold_checks():
     inv, wsp = 1, 3
     for bad in (-1.0, float("nan"), float("inf")):
