@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libnsortho.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["api.hip"] + [f"kern_{kind}_{t}.hip" for kind in ("sym", "nt")
-                         for t in ("f16_128", "f16_192", "f16_256", "f32_128")]
+                         for t in ("f16_128", "f16_192", "f16_256", "f32_128", "f32_64")]
 
 ARCH = "gfx950"
 

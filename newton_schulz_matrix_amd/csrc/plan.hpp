@@ -148,8 +148,16 @@ inline bool padding_fits(int64_t n_pad, int64_t m_pad, int esz) {
   return n_pad <= 65536 && m_pad * esz <= (int64_t(1) << 25);
 }
 
+// fp32 products: 128 tiles, or 64 when the n x n products would not fill
+// the chip with one wave of 128 tiles (small matrices, where a launch
+// otherwise keeps a handful of compute units busy).
+inline int pick_tile_fp32(int64_t n, int64_t batch) {
+  const int64_t t = (n + 127) / 128, ntri = t * (t + 1) / 2;
+  return ntri * batch < (int64_t)kComputeUnits ? 64 : 128;
+}
+
 inline int pick_tile(int64_t n, int64_t m, int64_t batch, ns_dtype internal, ns_mode mode) {
-  if (internal == NS_FP32) return 128;
+  if (internal == NS_FP32) return pick_tile_fp32(n, batch);
   int best = 128;
   double best_t = 0.0;
   for (const TileCost& c : kTileCosts) {
@@ -181,7 +189,8 @@ inline ns_status make_plan(int64_t rows, int64_t cols, int64_t batch, ns_dtype i
   p->n = p->transposed ? cols : rows;
   p->m = p->transposed ? rows : cols;
   const int req_tile = opt ? opt->tile : 0;
-  if (req_tile != 0 && !(req_tile == 128 || (internal != NS_FP32 && (req_tile == 192 || req_tile == 256))))
+  if (req_tile != 0 && !(req_tile == 128 || (internal != NS_FP32 && (req_tile == 192 || req_tile == 256)) ||
+                         (internal == NS_FP32 && req_tile == 64)))
     return NS_ERR_INVALID_ARG;
   p->tile = req_tile ? req_tile : pick_tile(p->n, p->m, batch, internal, mode);
   p->tile_n = nn_tile_n(p->tile);
@@ -816,7 +825,7 @@ ns_status run_typed(const Plan& p, const IoSpec& io, int steps, const float* a, 
   const float eps = opt ? opt->eps : 1e-7f;
   hipError_t e;
   if constexpr (sizeof(T) == 4) {
-    e = r.template run<128>(steps, a, b, c, eps);
+    e = p.tile == 64 ? r.template run<64>(steps, a, b, c, eps) : r.template run<128>(steps, a, b, c, eps);
   } else {
     switch (p.tile) {
       case 256: e = r.template run<256>(steps, a, b, c, eps); break;
@@ -846,6 +855,7 @@ NS_EXTERN_SYM(_Float16, 128)
 NS_EXTERN_SYM(_Float16, 192)
 NS_EXTERN_SYM(_Float16, 256)
 NS_EXTERN_SYM(float, 128)
+NS_EXTERN_SYM(float, 64)
 NS_EXTERN_NT(_Float16, _Float16, 128)
 NS_EXTERN_NT(_Float16, __bf16, 128)
 NS_EXTERN_NT(_Float16, _Float16, 192)
@@ -853,6 +863,7 @@ NS_EXTERN_NT(_Float16, __bf16, 192)
 NS_EXTERN_NT(_Float16, _Float16, 256)
 NS_EXTERN_NT(_Float16, __bf16, 256)
 NS_EXTERN_NT(float, float, 128)
+NS_EXTERN_NT(float, float, 64)
 #endif
 
 }  // namespace nsr

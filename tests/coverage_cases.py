@@ -41,8 +41,14 @@ CASES = [
     (1, 1300, 700, "fp16", 192),
     (1, 1300, 700, "fp16", 256),
     (1, 640, 512, "fp32", 0),
-    # fp32 single matrix with 264 update tiles of 32 k-tiles: persistent.
+    (1, 640, 512, "fp32", 128),
+    (1, 1300, 700, "fp32", 64),
+    # fp32 single matrices take 64 tiles while the n x n products would not
+    # fill the chip with 128 tiles; 1024 x 4224 has 1056 update tiles of 64
+    # (persistent), and forced to 128, 264 update tiles of 32 k-tiles
+    # (persistent too).
     (1, 1024, 4224, "fp32", 0),
+    (1, 1024, 4224, "fp32", 128),
 ]
 
 MODES = ("standard", "gram")

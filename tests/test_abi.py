@@ -141,15 +141,25 @@ def test_automatic_tile_choice():
     # kernels).
     assert _padded_n(300, 500) == 128
     assert _padded_n(2048, 1408, 128) == 128
-    # Forced tiles: fp32 products take 128 only; unknown edges are refused.
+    # Forced tiles: fp32 products take 64 or 128, 16-bit ones 128, 192 or
+    # 256; unknown edges are refused.
     lib = B.lib()
     for tile in (64, 200, 512):
         opt = B.make_options(tile=tile)
         assert lib.ns_workspace_size(512, 512, 1, B.NS_BF16, 0,
                                      ctypes.byref(opt)) == 0
-    opt = B.make_options(tile=192)
-    assert lib.ns_workspace_size(512, 512, 1, B.NS_FP32, 0,
-                                 ctypes.byref(opt)) == 0
+    for tile in (192, 256):
+        opt = B.make_options(tile=tile)
+        assert lib.ns_workspace_size(512, 512, 1, B.NS_FP32, 0,
+                                     ctypes.byref(opt)) == 0
+    # fp32 takes 64 tiles while the n x n products would have fewer than 256
+    # tiles of 128 (one wave on the chip): the 256 x 1024 matrix (3 tiles of
+    # 128, 10 of 64) and a batch of 12 512 x 1000 (120), not a batch of 40
+    # (400).
+    for (r, c, b), want in [((256, 1024, 1), 64), ((512, 1000, 12), 64),
+                            ((512, 1000, 40), 128), ((4096, 4096, 1), 128)]:
+        ks = nsa.plan_kernels(r, c, b, torch.float32, "gram")
+        assert ks[2].startswith(f"xxt<f32,{want},"), (r, c, b, ks)
 
 
 def test_workspace_size_rejects_bad_arguments():
@@ -306,12 +316,13 @@ def test_plan_kernels_names_the_builds():
     ks = nsa.plan_kernels(2048, 1408, 128, torch.bfloat16, "standard")
     assert ks[2:] == ["xxt<f16,128,pairloop>", "nn<f16,128,pairloop>",
                       "upd<f16,f16,128,pair,E>", "out<f16,bf16,128,pair,E>"]
-    # The naive Gram form has no restart update; fp32 takes 128 tiles and
-    # reads the a X term from global memory.
+    # The naive Gram form has no restart update; fp32
+    # reads the a X term from global memory (small fp32 matrices take 64
+    # tiles).
     ks = nsa.plan_kernels(300, 200, 1, torch.float32, "gram", restart_mask=0)
     assert not any(k.startswith("upd<") for k in ks)
     ks = nsa.plan_kernels(300, 200, 1, torch.float32, "standard")
-    assert "upd<f32,f32,128,tile,Eg>" in ks
+    assert "upd<f32,f32,64,tile,Eg>" in ks
     assert B.lib().ns_plan_kernels(0, 5, 1, 0, 0, 5, None, None, 0) == -1
 
 
