@@ -195,9 +195,12 @@ ns_status muon_impl(void* W, const void* G, float* M, int64_t batch, int64_t row
                                     reinterpret_cast<hipStream_t>(stream)});
 }
 
-// Soft-threshold workspace: select state + three histograms (kHistCopies copies each).
+// Soft-threshold workspace: select state + the histograms (three radix
+// passes of kHistCopies copies for fp32 keys, kSelCopies copies of all 2^15
+// keys for 16-bit ones).
 size_t threshold_ws_bytes() {
-  return align_up(sizeof(SelectState)) + align_up(3 * kHistCopies * kHistBins * sizeof(uint32_t));
+  return align_up(sizeof(SelectState)) +
+         align_up(std::max<size_t>(3 * kHistCopies * kHistBins, (size_t)kSelWords) * sizeof(uint32_t));
 }
 
 template <typename IO>
@@ -217,13 +220,19 @@ ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float 
   const int vec_clip = vec_hist && (reinterpret_cast<uintptr_t>(B) & 15) == 0 &&
                        (!O || (reinterpret_cast<uintptr_t>(O) & 15) == 0) ? 1 : 0;
   const uint64_t rank = (uint64_t)((numel + 1) / 2);
-  hipLaunchKernelGGL(k_select_init, dim3((3 * kHistCopies * kHistBins + 255) / 256), dim3(256), 0, st, state, hist,
-                     3 * kHistCopies * kHistBins,
-                     rank);
+  constexpr bool one_pass = sizeof(IO) == 2;
+  const int nhist = lambda >= 0.f ? 0 : one_pass ? kSelWords : 3 * kHistCopies * kHistBins;
+  hipLaunchKernelGGL(k_select_init, dim3((std::max(nhist, 1) + 255) / 256), dim3(256), 0, st, state, hist, nhist, rank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return NS_ERR_HIP;
   if (lambda >= 0.f) {
     hipLaunchKernelGGL(k_set_lambda, dim3(1), dim3(64), 0, st, state, lambda, d_lambda_out);
+  } else if constexpr (one_pass) {
+    // One block per compute unit (the LDS histogram takes 128 KiB).
+    const int64_t want = (numel + (int64_t)kSelThreads * 64 - 1) / ((int64_t)kSelThreads * 64);
+    const unsigned g = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 256));
+    hipLaunchKernelGGL((k_hist16<IO>), dim3(g), dim3(kSelThreads), 0, st, m, numel, hist, vec_hist);
+    hipLaunchKernelGGL((k_pick16<IO>), dim3(1), dim3(kSelThreads), 0, st, state, hist, mult, d_lambda_out);
   } else {
     constexpr int kb = KeyOf<IO>::kBits;
     // Digits from the top, at most 11 bits each.

@@ -5,13 +5,14 @@
 // with an l1 penalty and orthogonalizes only B.  The threshold is
 // lambda = mult * median|M| (mult = 3 in the heavy-tailed workload).
 //
-// The median is found exactly by a radix select on the bit patterns of |M|:
-// for IEEE formats, |x| compares like its bit pattern with the sign bit
-// cleared read as an unsigned integer.  Digits of up to 11 bits are taken
-// from the top; each pass histograms the digit of the keys that match the
-// prefix chosen so far (LDS histogram, merged with global atomics) and a
-// one-block kernel picks the bucket holding the wanted rank.  16-bit keys
-// (15 bits) take two passes, fp32 keys (31 bits) three.  No host sync.
+// The median is found exactly by a select on the bit patterns of |M|: for
+// IEEE formats, |x| compares like its bit pattern with the sign bit cleared
+// read as an unsigned integer.  16-bit keys (15 bits) take one histogram
+// pass over all 2^15 keys (k_hist16, k_pick16).  fp32 keys (31 bits) take a
+// radix select: digits of up to 11 bits from the top, each pass
+// histogramming the digit of the keys that match the prefix chosen so far
+// (LDS histogram, merged with global atomics), a one-block kernel picking
+// the bucket that holds the wanted rank; three passes.  No host sync.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -187,6 +188,144 @@ __global__ void __launch_bounds__(kHistThreads) k_radix_pick(SelectState* st, co
       st->lambda = lam;
       if (d_lambda_out) *d_lambda_out = lam;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One-pass select for 16-bit keys.  |x| of a bf16 or fp16 value is a 15-bit
+// key, so one histogram of all 2^15 keys finds the median exactly.  Every
+// work-group counts its share of the elements into a 128 KiB LDS histogram
+// and adds its nonzero bins into one of kSelCopies global copies (block b
+// into copy b % 8, the XCD it runs on, so a copy's atomics stay in that
+// XCD's L2), and the sums of each group of kSelGroup consecutive keys into
+// a small coarse histogram (copies likewise).  One block then scans the
+// coarse sums to find the group that holds the wanted rank and the group's
+// bins to find the key: it reads 2 K coarse sums and one group's bins
+// instead of all 8 x 32 K.
+// ---------------------------------------------------------------------------
+constexpr int kKeyBins16 = 1 << 15;
+constexpr int kSelCopies = 8;
+constexpr int kSelThreads = 1024;
+constexpr int kSelGroup = 128;                          // keys per coarse group
+constexpr int kSelGroups = kKeyBins16 / kSelGroup;      // 256
+constexpr int kSelFineWords = kSelCopies * kKeyBins16;  // fine histogram words, then the coarse ones
+constexpr int kSelWords = kSelFineWords + kSelCopies * kSelGroups;
+
+template <typename IO>
+__global__ void __launch_bounds__(kSelThreads) k_hist16(const IO* M, int64_t numel, uint32_t* hist, int vec_ok) {
+  __shared__ __attribute__((aligned(16))) uint32_t h[kKeyBins16];
+  for (int i = threadIdx.x; i < kKeyBins16 / 4; i += kSelThreads) reinterpret_cast<uint4*>(h)[i] = uint4{0, 0, 0, 0};
+  __syncthreads();
+  auto count = [&](uint32_t raw) { atomicAdd(&h[raw & 0x7fffu], 1u); };
+  auto count_chunk = [&](const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      count(w[j] & 0xffffu);
+      count(w[j] >> 16);
+    }
+  };
+  const int64_t tid = (int64_t)blockIdx.x * kSelThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kSelThreads;
+  int64_t done = 0;
+  if (vec_ok) {
+    const int64_t nvec = numel / 8;
+    const uint4* Mv = reinterpret_cast<const uint4*>(M);
+    int64_t i = tid;
+    // Eight 16-byte loads in flight per thread (128 KiB per compute unit):
+    // one round covers 16.7 M 16-bit elements on 256 blocks.
+    for (; i + 7 * stride < nvec; i += 8 * stride) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = Mv[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) count_chunk(v[u]);
+    }
+    for (; i < nvec; i += stride) count_chunk(Mv[i]);
+    done = nvec * 8;
+  }
+  for (int64_t i = done + tid; i < numel; i += stride) count((uint32_t)__builtin_bit_cast(uint16_t, M[i]));
+  __syncthreads();
+  // Flush: key k * kSelThreads + t for thread t (neighbouring lanes read
+  // neighbouring words, no LDS bank conflicts).  Nonzero bins also go into
+  // an LDS array of group totals, so each group costs one global atomic per
+  // work-group.
+  __shared__ uint32_t gsum[kSelGroups];
+  for (int i = threadIdx.x; i < kSelGroups; i += kSelThreads) gsum[i] = 0u;
+  __syncthreads();
+  const int copy = blockIdx.x % kSelCopies;
+  uint32_t* hg = hist + (int64_t)copy * kKeyBins16;
+  for (int k = 0; k < kKeyBins16 / kSelThreads; ++k) {
+    const int bin = k * kSelThreads + threadIdx.x;
+    const uint32_t c = h[bin];
+    if (c) {
+      atomicAdd(&hg[bin], c);
+      atomicAdd(&gsum[bin / kSelGroup], c);
+    }
+  }
+  __syncthreads();
+  uint32_t* coarse = hist + kSelFineWords + copy * kSelGroups;
+  for (int i = threadIdx.x; i < kSelGroups; i += kSelThreads)
+    if (gsum[i]) atomicAdd(&coarse[i], gsum[i]);
+}
+
+// One block: the key holding rank st->rank; lambda = mult * its value.
+template <typename IO>
+__global__ void __launch_bounds__(kSelThreads) k_pick16(SelectState* st, const uint32_t* hist, float mult,
+                                                       float* d_lambda_out) {
+  __shared__ uint64_t part[kSelThreads];
+  __shared__ int sh_group;
+  __shared__ uint64_t sh_before;
+  const uint64_t want = st->rank;
+  const int t = threadIdx.x;
+  // Coarse pass: thread t < 256 holds group t's total over the copies.
+  uint64_t s = 0;
+  if (t < kSelGroups) {
+#pragma unroll
+    for (int k = 0; k < kSelCopies; ++k) s += hist[kSelFineWords + k * kSelGroups + t];
+  }
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    const uint64_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  {
+    const uint64_t incl = part[t], excl = incl - s;
+    if (t < kSelGroups && ((excl < want && want <= incl) || (t == kSelGroups - 1 && want > incl))) {
+      sh_group = t;
+      sh_before = excl;
+    }
+  }
+  __syncthreads();
+  const int g = sh_group;
+  const uint64_t before = sh_before;
+  // Fine pass over the group's keys: thread t < 128 holds key g*128 + t.
+  uint64_t c = 0;
+  if (t < kSelGroup) {
+#pragma unroll
+    for (int k = 0; k < kSelCopies; ++k) c += hist[(int64_t)k * kKeyBins16 + g * kSelGroup + t];
+  }
+  __syncthreads();
+  part[t] = c;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    const uint64_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  const uint64_t incl = before + part[t], excl = incl - c;
+  if (t < kSelGroup && ((excl < want && want <= incl) || (t == kSelGroup - 1 && want > incl))) {
+    const uint32_t key = (uint32_t)(g * kSelGroup + t);
+    st->rank = want - excl;
+    st->prefix = key;
+    st->mask = 0x7fffu;
+    const float lam = mult * KeyOf<IO>::value(key);
+    st->lambda = lam;
+    if (d_lambda_out) *d_lambda_out = lam;
   }
 }
 
