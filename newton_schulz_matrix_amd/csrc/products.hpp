@@ -205,7 +205,12 @@ struct FragAddr {
   uint32_t row0L, row0R;  // (w0 + (L & 31)) * 128 for the L and R operands
   int swL0, swL1, swR0, swR1;  // swz for even and odd i
   __device__ __forceinline__ void init(int wr, int wc) {
-    const int lr = threadIdx.x & 31;
+    // The lane index goes through an opaque move so that a persistent kernel
+    // recomputes these offsets per tile: hoisted out of its tile loop they
+    // stay live across the main loop and are spilled at two work-groups per
+    // compute unit.
+    int lr;
+    asm volatile("v_and_b32 %0, 31, %1" : "=v"(lr) : "v"((int)threadIdx.x));
     row0L = (uint32_t)((wr + lr) * kRowBytes);
     row0R = (uint32_t)((wc + lr) * kRowBytes);
     swL0 = swz(wr + lr);
