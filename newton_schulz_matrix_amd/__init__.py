@@ -13,7 +13,8 @@ from .flops import gram_flops, ns_flops, standard_flops
 from ._binding import (NS_MAX_STEPS, TUNED_ABC, NSError, lib, muon_step,
                        muon_workspace_size, orthogonalize,
                        orthogonalize_batched, orthogonalize_grouped,
-                       grouped_workspace_size, plan_kernels,
+                       orthogonalize_static, grouped_workspace_size,
+                       plan_kernels,
                        soft_threshold_split, status_code, status_string,
                        workspace_size)
 from .coeffs import fit_coefficients, root_coefficients
@@ -21,7 +22,7 @@ from .coeffs import fit_coefficients, root_coefficients
 __all__ = [
     "NS_MAX_STEPS", "TUNED_ABC", "NSError", "lib", "muon_step",
     "muon_workspace_size", "orthogonalize",
-    "orthogonalize_batched", "orthogonalize_grouped",
+    "orthogonalize_batched", "orthogonalize_grouped", "orthogonalize_static",
     "grouped_workspace_size", "plan_kernels", "soft_threshold_split",
     "status_code", "status_string",
     "workspace_size", "gram_flops", "ns_flops", "standard_flops",
