@@ -36,6 +36,12 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 inline int elem_size(ns_dtype d) { return d == NS_FP32 ? 4 : 2; }
 
+// A launch of the two-work-groups-per-CU kernels (the large batches) that
+// writes more than this many bytes takes their build with non-temporal
+// stores (the MI355X MALL holds 256 MiB; see store16).
+constexpr double kStreamOutBytes = 256.0 * 1024 * 1024;
+inline int stream_out(double written_bytes) { return written_bytes > kStreamOutBytes ? 1 : 0; }
+
 // Shapes and workspace layout of one call.
 struct Plan {
   int64_t rows = 0, cols = 0, n = 0, m = 0, n_pad = 0, m_pad = 0;
@@ -318,13 +324,22 @@ hipError_t launch_sym_g(SymArgs<T> a, int64_t batch, hipStream_t s, LaunchEvents
   a.batch = (int)batch;
   switch (sym_form(TILE, (int)sizeof(T), ntri * batch, ktiles)) {
     case Form::kPairLoop:
-      if constexpr (kHasPairKernels<T, TILE>)
+      if constexpr (kHasPairKernels<T, TILE>) {
+        if constexpr (!EXT)
+          if (a.stream_out)
+            return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2, false, true>, dim3(2 * kPersistentGroups),
+                                 dim3(kThreads), s, ev, a);
         return launch_kernel(k_sym_loop<T, TILE, GRAM_INPUT, 2, EXT>, dim3(2 * kPersistentGroups), dim3(kThreads), s,
                              ev, a);
+      }
       break;
     case Form::kPairTile:
-      if constexpr (kHasPairKernels<T, TILE>)
+      if constexpr (kHasPairKernels<T, TILE>) {
+        if constexpr (!EXT)
+          if (a.stream_out)
+            return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2, false, true>, tiles_grid, dim3(kThreads), s, ev, a);
         return launch_kernel(k_sym<T, TILE, GRAM_INPUT, 2, EXT>, tiles_grid, dim3(kThreads), s, ev, a);
+      }
       break;
     case Form::kLoop:
       if constexpr (TILE <= 192)
@@ -353,8 +368,12 @@ hipError_t launch_nt_g(NTArgs<T, OutT> a, int64_t batch, hipStream_t s, LaunchEv
   a.batch = (int)batch;
   switch (nt_form(TILE, (int)sizeof(T), per * batch, a.K / (kRowBytes / (int)sizeof(T)))) {
     case Form::kPairTile:
-      if constexpr (kHasPairKernels<T, TILE>)
+      if constexpr (kHasPairKernels<T, TILE>) {
+        if constexpr (!EXT)
+          if (a.stream_out)
+            return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP, false, true>, flat, dim3(kThreads), s, ev, a);
         return launch_kernel(k_nt<T, OutT, TILE, TN, 2, CAP, EXT>, flat, dim3(kThreads), s, ev, a);
+      }
       break;
     case Form::kLoop:
       if constexpr (TILE <= 192)
@@ -463,6 +482,7 @@ struct Runner {
     a.xsel = g.xsel ? flags() : nullptr;
     a.x_alt = xbuf(1) - xbuf(0);
     a.flag_stride = kFlagStride;
+    a.stream_out = stream_out((double)p.batch * (double)p.nn_elems * sizeof(T) * (C2 ? 2.0 : 1.0));
     const double n = (double)p.n, bt = (double)p.batch, es = sizeof(T);
     const double inner = gram ? (double)p.m : n;
     const double flops = n * n * inner * bt;
@@ -530,6 +550,7 @@ struct Runner {
     a.y_alt = xbuf(1) - xbuf(0);
     a.yt_alt = xtbuf(1) - xtbuf(0);
     a.flag_stride = kFlagStride;
+    a.stream_out = stream_out(2.0 * (double)p.batch * (double)p.x_elems * sizeof(T));
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (3.0 + (with_e ? 1.0 : 0.0)));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
@@ -577,6 +598,7 @@ struct Runner {
     a.yt_alt = 0;
     a.flag_stride = kFlagStride;
     a.members = members;
+    a.stream_out = stream_out((double)p.batch * (double)p.rows * (double)p.cols * sizeof(IO));
     const double n = (double)p.n, m = (double)p.m, bt = (double)p.batch, es = sizeof(T);
     const double bytes = bt * (n * n * es + n * m * es * (1.0 + (with_e ? 1.0 : 0.0)) + n * m * sizeof(IO));
     return tr.run(NS_KERNEL_UPDATE, 2.0 * n * n * m * bt, bytes,
@@ -769,6 +791,61 @@ inline std::string describe_plan(const Plan& p, int steps, uint32_t mask, bool g
   // Updates with an E term capture it from LDS where the tile has the
   // registers (16-bit, edges up to 192), else read it from global memory.
   const std::string e_term = esz == 2 && p.tile <= 192 ? ",E" : ",Eg";
+  const Form fx = sym_form(p.tile, esz, ntri, km), fn = sym_form(p.tile, esz, ntri, kn),
+             fu = nt_form(p.tile, esz, nt_tiles, kn);
+  // ",nt": the build with non-temporal stores, which a launch of a
+  // two-work-groups-per-CU kernel without extended arguments takes when it
+  // writes more than kStreamOutBytes (see launch_sym_g, launch_nt_g).
+  const double bt = (double)p.batch, nn_bytes = bt * (double)p.nn_elems * esz;
+  const double x2_bytes = 2.0 * bt * (double)p.x_elems * esz;
+  const double out_bytes = bt * (double)p.rows * (double)p.cols * elem_size(p.io);
+  auto ntag = [](Form f, bool ext, double bytes) {
+    return (f == Form::kPairLoop || f == Form::kPairTile) && !ext && stream_out(bytes) ? std::string(",nt")
+                                                                                       : std::string();
+  };
+  auto xxt = [&](bool ext) { return "xxt<" + T + "," + E + "," + form_name(fx) + ntag(fx, ext, nn_bytes) + ">"; };
+  auto nn = [&](bool ext, bool c2) {
+    return "nn<" + T + "," + E + "," + form_name(fn) + ntag(fn, ext, nn_bytes * (c2 ? 2.0 : 1.0)) + ">";
+  };
+  auto upd = [&](bool ext, const std::string& et) {
+    return "upd<" + T + "," + T + "," + E + "," + form_name(fu) + et + ntag(fu, ext, x2_bytes) + ">";
+  };
+  auto fin = [&](bool ext, const std::string& et) {
+    return "out<" + T + "," + IO + "," + E + "," + form_name(fu) + et + ntag(fu, ext, out_bytes) + ">";
+  };
+  // The launches of one call, in the order of the runner (Runner::run and
+  // Runner::run_guarded), by kind.
+  std::vector<std::string> xs, ns, us;
+  std::string fo;
+  if (p.mode == NS_STANDARD) {
+    xs.push_back(xxt(false));
+    ns.push_back(nn(false, false));
+    if (steps > 1) us.push_back(upd(false, e_term));
+    fo = fin(false, e_term);
+  } else if (guard) {
+    // Every launch reads the guard's flags except the first step's Z'
+    // product, which writes the fresh Q.
+    xs.push_back(xxt(true));
+    ns.push_back(nn(false, true));
+    if (steps > 1) {
+      us.push_back(upd(true, ",noE"));
+      ns.push_back(nn(true, false));
+    }
+    fo = fin(true, ",noE");
+  } else {
+    xs.push_back(xxt(false));
+    bool fresh = true;
+    for (int k = 1; k <= steps; ++k) {
+      if (k > 1 && ((mask >> k) & 1u)) {
+        us.push_back(upd(false, ",noE"));
+        fresh = true;
+      }
+      ns.push_back(nn(false, fresh));
+      if (!fresh || (k < steps && !((mask >> (k + 1)) & 1u))) ns.push_back(nn(false, false));
+      fresh = false;
+    }
+    fo = fin(false, ",noE");
+  }
   std::vector<std::string> seen;
   std::string out;
   auto add = [&](const std::string& v) {
@@ -778,19 +855,10 @@ inline std::string describe_plan(const Plan& p, int steps, uint32_t mask, bool g
   };
   add("sumsq<" + IO + ">");
   add("stage<" + IO + "," + T + ">");
-  const std::string xxt = "xxt<" + T + "," + E + "," + form_name(sym_form(p.tile, esz, ntri, km)) + ">";
-  const std::string nn = "nn<" + T + "," + E + "," + form_name(sym_form(p.tile, esz, ntri, kn)) + ">";
-  const std::string upd = std::string(form_name(nt_form(p.tile, esz, nt_tiles, kn)));
-  add(xxt);
-  add(nn);
-  if (p.mode == NS_STANDARD) {
-    if (steps > 1) add("upd<" + T + "," + T + "," + E + "," + upd + e_term + ">");
-    add("out<" + T + "," + IO + "," + E + "," + upd + e_term + ">");
-  } else {
-    for (int k = 2; k <= steps; ++k)
-      if (guard || ((mask >> k) & 1u)) add("upd<" + T + "," + T + "," + E + "," + upd + ",noE>");
-    add("out<" + T + "," + IO + "," + E + "," + upd + ",noE>");
-  }
+  for (const auto& v : xs) add(v);
+  for (const auto& v : ns) add(v);
+  for (const auto& v : us) add(v);
+  add(fo);
   return out;
 }
 

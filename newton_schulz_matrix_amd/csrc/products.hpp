@@ -40,8 +40,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "../../include/nsortho.h"
 
 namespace nsk {
@@ -529,6 +527,7 @@ struct SymArgs {
   const int32_t* xsel;
   int64_t x_alt;
   int32_t gate_want, flag_stride;
+  int stream_out;  // 1: the launcher takes the build with non-temporal stores (see store16)
 };
 
 // A guarded launch computes matrix bz's tiles only when its flag matches.
@@ -571,6 +570,7 @@ struct NTArgs {
   // members[bz].data with leading dimension members[bz].ld, transposed when
   // members[bz].transposed; Y, sY, ldy and transpose_out are then unused.
   const ns_matrix* members;
+  int stream_out;  // 1: the launcher takes the build with non-temporal stores (see store16)
 };
 
 // Ors `bits` into the status word once per wave in which some lane saw a
@@ -580,9 +580,32 @@ __device__ __forceinline__ void report_status(int32_t* d_status, int32_t bits, b
   if (any_bad && (int)(threadIdx.x & 63) == __ffsll(any_bad) - 1) atomicOr(d_status, bits);
 }
 
+// One 16-byte store of an epilogue, non-temporal in the STREAM builds.  The
+// launcher takes those when one launch writes more than the MALL holds: the
+// output would not stay cached for the next kernel anyway and only displaces
+// operands still in use.  Same-box A/B: the 128-expert MoE batch 3.0 %
+// (Gram form) and 2.4 % (standard) faster per call; non-temporal stores in
+// every launch made a 2048 x 8192 call, whose 8 MB state does stay cached,
+// 17 % slower, and 48 matrices of 768 x 768 7 % slower.
+// The choice is a template argument of the kernel build (STREAM): behind a
+// run-time test of each store the compiler merged the two stores into one
+// plain store, and an epilogue instantiated for both kinds in one build
+// spilled in the two-work-groups-per-CU kernels.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <bool STREAM>
+__device__ __forceinline__ void store16(void* dst, const uint4& v) {
+  if constexpr (STREAM) {
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(dst));
+  } else {
+    *reinterpret_cast<uint4*>(dst) = v;
+  }
+}
+
+
 // The caller's 16-byte chunk `dst` gets `val` (kEC rounded results), or
 // with `acc`, dst + s * val computed in fp32 and rounded once more.
-template <typename OutT>
+template <bool STREAM, typename OutT>
 __device__ __forceinline__ void final_chunk(OutT* dst, uint4 val, int acc, float s) {
   if (acc) {
     constexpr int kEC = 16 / (int)sizeof(OutT);
@@ -592,7 +615,7 @@ __device__ __forceinline__ void final_chunk(OutT* dst, uint4 val, int acc, float
 #pragma unroll
     for (int e = 0; e < kEC; ++e) v[e] = from_f32<OutT>(fmaf(s, to_f32<OutT>(v[e]), to_f32<OutT>(o[e])));
   }
-  *reinterpret_cast<uint4*>(dst) = val;
+  store16<STREAM>(dst, val);
 }
 template <typename OutT>
 __device__ __forceinline__ void final_elem(OutT* dst, OutT val, int acc, float s) {
@@ -893,7 +916,7 @@ __device__ __forceinline__ uint4 with_elem(uint4 v, int k, T d) {
 // iteration's device flags; for updates also the member table of a grouped
 // call); other launches take the build without that code (it changed the
 // schedule of the products enough to cost 6 % of a call).
-template <typename T, int TILE, int G, bool EXT>
+template <typename T, int TILE, int G, bool EXT, bool STREAM>
 __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, int bz) {
   using A = Acc<T, TILE, TILE>;
   constexpr int FM = A::FM, FN = A::FN;
@@ -974,14 +997,15 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
   // tile takes every element from its upper triangle, so the stored matrix
   // is exactly symmetric: here it writes only the chunks right of its
   // diagonal blocks, and phase C the rest.
+  constexpr bool S = STREAM;
 #pragma unroll 6
   for (int it = 0; it < kChunks / kThreads; ++it) {
     const int q = it * kThreads + threadIdx.x;
     const int r = q / TL::kCPR, c = q % TL::kCPR;
     if (!diag_tile || c > r / EC) {
       const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
-      *reinterpret_cast<uint4*>(C + (row0 + r) * p.ldn + col0 + c * EC) = val;
-      if (C2) *reinterpret_cast<uint4*>(C2 + (row0 + r) * p.ldn + col0 + c * EC) = val;
+      store16<S>(C + (row0 + r) * p.ldn + col0 + c * EC, val);
+      if (C2) store16<S>(C2 + (row0 + r) * p.ldn + col0 + c * EC, val);
     }
   }
 
@@ -1010,11 +1034,10 @@ __device__ __forceinline__ void sym_tile(const SymArgs<T>& p, int tm, int tn, in
 #pragma unroll
       for (int e = 0; e < EC; ++e) {
         const int64_t off = (col0 + cb * EC + e) * p.ldn + row0 + rb * EC;
-        *reinterpret_cast<uint4*>(C + off) = cols[e];
+        store16<S>(C + off, cols[e]);
         if (C2) {
           const int rr = rb * EC + e;
-          *reinterpret_cast<uint4*>(C2 + off) =
-              on_diag && row0 + rr < p.n_real ? with_elem<T>(cols[e], e, c2d[rr]) : cols[e];
+          store16<S>(C2 + off, on_diag && row0 + rr < p.n_real ? with_elem<T>(cols[e], e, c2d[rr]) : cols[e]);
         }
       }
     }
@@ -1029,19 +1052,19 @@ __device__ __forceinline__ int persistent_piece(int b, int G) { return (b % kXcd
 // GRAM_INPUT only separates the X X^T launches (inner dimension m) from the
 // n x n products into their own kernel symbol, so profiles list them apart.
 // One work-group per upper-triangle tile.
-template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool EXT = false>
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool EXT = false, bool STREAM = false>
 __global__ void __launch_bounds__(kThreads, G) k_sym(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   int tm, tn;
   tri_tile(gridDim.y == 1 ? xcd_order(blockIdx.x, ntri) : blockIdx.x, p.tiles, tm, tn);
-  sym_tile<T, TILE, G, EXT>(p, tm, tn, blockIdx.y);
+  sym_tile<T, TILE, G, EXT, STREAM>(p, tm, tn, blockIdx.y);
 }
 
 // Persistent form: a grid of work-groups looping over the tiles of all
 // matrices in list order, so one tile's stores drain while the next one
 // starts.  A kernel of its own: the loop's live state would push the 256
 // tile past the register file.
-template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool EXT = false>
+template <typename T, int TILE, bool GRAM_INPUT, int G = 1, bool EXT = false, bool STREAM = false>
 __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
   const int ntri = p.tiles * (p.tiles + 1) / 2;
   const int total = ntri * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
@@ -1049,7 +1072,7 @@ __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
     const int pos = base + piece, bz = pos / ntri;
     int tm, tn;
     tri_tile(pos % ntri, p.tiles, tm, tn);
-    sym_tile<T, TILE, G, EXT>(p, tm, tn, bz);
+    sym_tile<T, TILE, G, EXT, STREAM>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }
@@ -1057,7 +1080,7 @@ __global__ void __launch_bounds__(kThreads, G) k_sym_loop(SymArgs<T> p) {
 // Y = alpha E + gamma B (X^T)^T on TM x TN tiles: the update of both forms.
 // CAP: E is taken from the X^T panel in LDS during the main loop; otherwise
 // it is loaded from global memory before the main loop (or absent).
-template <typename T, typename OutT, int TM, int TN, int G, bool CAP, bool EXT>
+template <typename T, typename OutT, int TM, int TN, int G, bool CAP, bool EXT, bool STREAM>
 __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn, int bz) {
   using A = Acc<T, TM, TN>;
   constexpr int FM = A::FM, FN = A::FN;
@@ -1155,6 +1178,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
   // take consecutive rb, so a transposed row is written as adjacent chunks.
   constexpr int kRB = TM / kEC, kBlocks = kRB * TL::kCPR;
   constexpr int kBIters = (kBlocks + kThreads - 1) / kThreads;
+  constexpr bool S = STREAM;
   if (!p.final_out) {
     // Internal buffers: the whole padded tile, rows of Y and, when asked,
     // rows of Y^T (columns of the tile).
@@ -1162,8 +1186,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
     for (int it = 0; it < kChunks / kThreads; ++it) {
       const int q = it * kThreads + threadIdx.x;
       const int r = q / TL::kCPR, c = q % TL::kCPR;
-      *reinterpret_cast<uint4*>(Y + (row0 + r) * ldy + col0 + c * kEC) =
-          *reinterpret_cast<const uint4*>(TL::chunk(r, c));
+      store16<S>(Y + (row0 + r) * ldy + col0 + c * kEC, *reinterpret_cast<const uint4*>(TL::chunk(r, c)));
     }
     if (YT) {
 #pragma unroll 1
@@ -1175,7 +1198,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
           TL::block_t(rb, cb, cols);
 #pragma unroll
           for (int e = 0; e < kEC; ++e)
-            *reinterpret_cast<uint4*>(YT + (col0 + cb * kEC + e) * p.ldyt + row0 + rb * kEC) = cols[e];
+            store16<S>(YT + (col0 + cb * kEC + e) * p.ldyt + row0 + rb * kEC, cols[e]);
         }
       }
     }
@@ -1191,7 +1214,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
       const uint4 val = *reinterpret_cast<const uint4*>(TL::chunk(r, c));
       OutT* dst = Y + i * ldy + j0;
       if (vec && j0 + kEC <= p.m_real) {
-        final_chunk(dst, val, p.accumulate, p.apply_scale);
+        final_chunk<S>(dst, val, p.accumulate, p.apply_scale);
       } else {
         const OutT* vals = reinterpret_cast<const OutT*>(&val);
         for (int e = 0; e < kEC && j0 + e < p.m_real; ++e) final_elem(dst + e, vals[e], p.accumulate, p.apply_scale);
@@ -1216,7 +1239,7 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
         if (j >= p.m_real) continue;
         OutT* dst = Y + j * ldy + i0;
         if (vec && i0 + kEC <= p.n_real) {
-          final_chunk(dst, cols[e], p.accumulate, p.apply_scale);
+          final_chunk<S>(dst, cols[e], p.accumulate, p.apply_scale);
         } else {
           const OutT* vals = reinterpret_cast<const OutT*>(&cols[e]);
           for (int k = 0; k < kEC && i0 + k < p.n_real; ++k) final_elem(dst + k, vals[k], p.accumulate, p.apply_scale);
@@ -1230,17 +1253,19 @@ __device__ __forceinline__ void nt_tile(const NTArgs<T, OutT>& p, int tm, int tn
 // One work-group per tile on a one-dimensional grid over the tiles of all
 // matrices: the list (matrix by matrix, each in grouped_tile order) is cut
 // into one contiguous piece per XCD.
-template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool EXT = false>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool EXT = false,
+          bool STREAM = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int pos = xcd_order(blockIdx.x, per * p.batch);
   int tm, tn;
   grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-  nt_tile<T, OutT, TM, TN, G, CAP, EXT>(p, tm, tn, pos / per);
+  nt_tile<T, OutT, TM, TN, G, CAP, EXT, STREAM>(p, tm, tn, pos / per);
 }
 
 // Persistent form of k_nt (see k_sym_loop).
-template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool EXT = false>
+template <typename T, typename OutT, int TM, int TN, int G = 1, bool CAP = false, bool EXT = false,
+          bool STREAM = false>
 __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
   const int per = p.tiles_m * p.tiles_n;
   const int total = per * p.batch, groups = gridDim.x, piece = persistent_piece(blockIdx.x, groups);
@@ -1248,7 +1273,7 @@ __global__ void __launch_bounds__(kThreads, G) k_nt_loop(NTArgs<T, OutT> p) {
     const int pos = base + piece, bz = pos / per;
     int tm, tn;
     grouped_tile(pos % per, p.tiles_m, p.tiles_n, tm, tn);
-    nt_tile<T, OutT, TM, TN, G, CAP, EXT>(p, tm, tn, bz);
+    nt_tile<T, OutT, TM, TN, G, CAP, EXT, STREAM>(p, tm, tn, bz);
     lds_barrier();  // the next tile's copies reuse the LDS the epilogue read
   }
 }

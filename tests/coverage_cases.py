@@ -32,6 +32,13 @@ CASES = [
     # kernels with one work-group per tile (650 upper tiles, 50 and 52
     # k-tiles).
     (2, 3200, 3300, "bf16", 128),
+    # The same kernels writing more than 256 MiB per launch take their builds
+    # with non-temporal stores: 16 x 3200 x 3300 (328 MB per n x n product),
+    # and the MoE batch (128 x 1408 x 1408: 507 MB per n x n product,
+    # persistent) for both 16-bit I/O types.
+    (16, 3200, 3300, "bf16", 128),
+    (128, 2048, 1408, "bf16", 0),
+    (128, 1408, 2048, "fp16", 0),
     # One work-group per tile at every edge, both 16-bit I/O types (ragged
     # in both directions; tall, so the result is transposed back).
     (1, 1300, 700, "bf16", 128),

@@ -313,9 +313,17 @@ def test_plan_kernels_names_the_builds():
     assert ks == ["sumsq<bf16>", "stage<bf16,f16>", "xxt<f16,192,tile>",
                   "nn<f16,192,tile>", "upd<f16,f16,192,tile,noE>",
                   "out<f16,bf16,192,tile,noE>"]
+    # The MoE batch writes more than 256 MiB per launch: the builds with
+    # non-temporal stores (",nt").
     ks = nsa.plan_kernels(2048, 1408, 128, torch.bfloat16, "standard")
-    assert ks[2:] == ["xxt<f16,128,pairloop>", "nn<f16,128,pairloop>",
-                      "upd<f16,f16,128,pair,E>", "out<f16,bf16,128,pair,E>"]
+    assert ks[2:] == ["xxt<f16,128,pairloop,nt>", "nn<f16,128,pairloop,nt>",
+                      "upd<f16,f16,128,pair,E,nt>", "out<f16,bf16,128,pair,E,nt>"]
+    ks = nsa.plan_kernels(768, 768, 48, torch.bfloat16, "gram")
+    assert not any(k.endswith(",nt>") for k in ks)
+    # Five 4096 x 4096 matrices: only the n x n launch that also writes the
+    # fresh Q (2 x 168 MB) passes the limit.
+    ks = nsa.plan_kernels(4096, 4096, 5, torch.bfloat16, "gram", tile=128)
+    assert "nn<f16,128,pair,nt>" in ks and "nn<f16,128,pair>" in ks
     # The naive Gram form has no restart update; fp32
     # reads the a X term from global memory (small fp32 matrices take 64
     # tiles).
