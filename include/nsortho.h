@@ -366,7 +366,7 @@ ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch,
  * The kernel builds one call would launch, for inspection (host only;
  * touches no device).  Arguments as for ns_workspace_size, plus the step
  * count.  Writes a NUL-terminated, space-separated list of the distinct
- * builds in launch order into buf (truncated to len bytes; buf may be NULL)
+ * builds (see below for the order) into buf (truncated to len bytes; buf may be NULL)
  * and returns the length the whole list needs including the NUL, or -1 for
  * invalid arguments.  Entries: sumsq<io>, stage<io,op>; xxt<op,tile,form>
  * (X X^T) and nn<op,tile,form> (n x n products); upd<op,op,tile,form,e>
@@ -375,6 +375,12 @@ ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch,
  * loop (a persistent grid), pair and pairloop (the same, built for two
  * work-groups per compute unit), e is E when the a X term is taken from
  * LDS, Eg when it is read from global memory and noE when there is none.
+ * A trailing ",nt" marks the pair/pairloop builds whose output stores are
+ * non-temporal, taken by a launch that writes more than 256 MiB (the
+ * MI355X MALL's size) and reads no guard flags or member table.  The list
+ * follows the call's launches by kind: the norm and staging passes, the
+ * X X^T builds, the n x n builds, the intermediate updates, the final
+ * product.
  */
 int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch,
                         ns_dtype dtype, ns_mode mode, int32_t steps,
