@@ -35,6 +35,11 @@ come from the oracle itself):
   printed 2048 x 2048 orthogonalization MSE; equivariance invariants.
 * ``ns_gram``: equals ``ns_standard`` in fp64 (with and without restart) and
   matches the same closed form.
+* ``gram_iterate``: the recurrence ``ns_gram`` runs; started from a Gram
+  matrix with one eigenvalue made negative, its action along that
+  eigenvector matches the scalar recurrence mu <- mu (a + b mu + c mu^2)^2
+  (the naive iteration grows it without bound), and a restart brings the
+  result back into the scalar map's band.
 * ``jacobi_svd`` / ``polar_jacobi``: against ``numpy.linalg.svd`` and the
   defining properties (orthonormal factors, reconstruction).
 * ``polar_eigh``: against ``polar_jacobi`` and the isometry property.
@@ -49,14 +54,14 @@ No function here is "parity unpinned".
 """
 
 from .ns import (CLASSIC_ABC, TUNED_ABC, coefficient_schedule, frobenius_stage,
-                 ns_gram, ns_standard, scalar_map)
+                 gram_iterate, ns_gram, ns_standard, scalar_map)
 from .svd import jacobi_svd, polar_eigh, polar_jacobi, orthogonalization_mse
 from .soft_threshold import lower_median_abs, soft_threshold_split
 from .muon import momentum_update, muon_step
 
 __all__ = [
     "CLASSIC_ABC", "TUNED_ABC", "coefficient_schedule", "frobenius_stage",
-    "ns_gram", "ns_standard", "scalar_map", "jacobi_svd", "polar_eigh",
+    "gram_iterate", "ns_gram", "ns_standard", "scalar_map", "jacobi_svd", "polar_eigh",
     "polar_jacobi", "orthogonalization_mse", "lower_median_abs",
     "soft_threshold_split", "momentum_update", "muon_step",
 ]

@@ -123,13 +123,26 @@ def ns_gram(m: np.ndarray, steps: int = 5,
     ``restart`` holds 1-based step numbers; a restart before step 1 is a
     no-op.  Returns Q X, oriented like the input.
     """
-    restart = set(int(k) for k in restart)
     x, transposed = frobenius_stage(m, eps)
+    out = gram_iterate(x, x @ x.T, coefficient_schedule(abc, steps), restart)
+    return out.T if transposed else out
+
+
+def gram_iterate(x: np.ndarray, r: np.ndarray, sched: Sequence[Triple],
+                 restart: Iterable[int] = (4,)) -> np.ndarray:
+    """The Gram recurrence from a given start: Q X after ``len(sched)`` steps.
+
+    ``x`` is the wide, normalized iterate and ``r`` the Gram matrix the
+    iteration starts from (X X^T for ns_gram).  Taking ``r`` as an argument
+    lets a test start from a Gram matrix that lost positive
+    semi-definiteness, the failure the Gram-NS article describes for naive
+    Gram iterations in float16 ("Stability challenges and solutions"); a
+    restart recomputes R from X and so discards it.
+    """
+    restart = set(int(k) for k in restart)
     n = x.shape[0]
     eye = np.eye(n)
-    r = x @ x.T
     q = eye.copy()
-    sched = coefficient_schedule(abc, steps)
     for k, (a, b, c) in enumerate(sched, start=1):
         if k in restart and k > 1:
             x = q @ x
@@ -138,5 +151,4 @@ def ns_gram(m: np.ndarray, steps: int = 5,
         z = a * eye + b * r + c * (r @ r)
         q = z @ q
         r = z @ r @ z
-    out = q @ x
-    return out.T if transposed else out
+    return q @ x

@@ -13,7 +13,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (CLASSIC_ABC, TUNED_ABC, jacobi_svd, lower_median_abs,
+from oracle import (CLASSIC_ABC, TUNED_ABC, frobenius_stage, gram_iterate,
+                    jacobi_svd, lower_median_abs,
                     momentum_update, muon_step, ns_gram, ns_standard,
                     orthogonalization_mse, polar_eigh, polar_jacobi,
                     scalar_map, soft_threshold_split)
@@ -141,6 +142,58 @@ def test_gram_equals_standard(restart):
 def test_gram_equals_standard_tall_bf16_input():
     m = workloads.gaussian((200, 64), seed=9, dtype="bf16").double().numpy()
     assert _rel(ns_gram(m), ns_standard(m)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# The failure of naive Gram iterations ([Gram-NS], "Stability challenges and
+# solutions"): a Gram matrix that lost positive semi-definiteness.  Its
+# smallest eigenvalue is replaced by mu < 0 (same eigenvector u); every matrix
+# of the recurrence is then a polynomial in that R, so along u the iteration
+# is the scalar recurrence  w_k = a + b mu_k + c mu_k^2,  mu_{k+1} = mu_k w_k^2,
+# with Q multiplied by w_k.  For mu < 0 every term of w_k is positive and
+# mu_k runs off to minus infinity.
+# ---------------------------------------------------------------------------
+
+def _negative_gram(mu):
+    m = workloads.gaussian((48, 160), seed=21, dtype="fp64").numpy()
+    x, _ = frobenius_stage(m)
+    r = x @ x.T
+    lam, vec = np.linalg.eigh(r)
+    u = vec[:, 0]
+    return x, r + (mu - lam[0]) * np.outer(u, u), u
+
+
+def test_naive_gram_from_a_negative_eigenvalue_follows_the_scalar_recurrence():
+    mu0 = -1e-3
+    x, r_bad, u = _negative_gram(mu0)
+    sched = [TUNED_ABC] * 5
+    out = gram_iterate(x, r_bad, sched, restart=())
+    q_u, mu = 1.0, mu0
+    for a, b, c in sched:
+        w = a + b * mu + c * mu * mu
+        q_u, mu = q_u * w, mu * w * w
+    assert q_u > 1e9
+    # Along u the result is q_u times X's component; elsewhere R is
+    # untouched, so the rest equals the ordinary naive iteration.
+    assert abs(float(u @ out @ (x.T @ u)) / float(u @ x @ x.T @ u) - q_u) < 1e-9 * q_u
+    good = gram_iterate(x, x @ x.T, sched, restart=())
+    proj = np.eye(len(u)) - np.outer(u, u)
+    # fp64 rounding of the products leaks about eps * q_u of the huge
+    # component along u into the others.
+    assert _rel(proj @ out, proj @ good) < 1e-15 * q_u
+    assert np.linalg.norm(out, 2) > 1e3
+
+
+def test_restart_discards_the_negative_eigenvalue():
+    x, r_bad, _ = _negative_gram(-1e-3)
+    sched = [TUNED_ABC] * 5
+    # A restart before step 2 recomputes R from X after one step: the
+    # result is back in the band of the ordinary iteration.
+    out = gram_iterate(x, r_bad, sched, restart=(2,))
+    s = np.linalg.svd(out, compute_uv=False)
+    assert np.all(np.isfinite(s)) and s.max() < 1.3
+    ref = np.linalg.svd(gram_iterate(x, x @ x.T, sched, restart=(2,)), compute_uv=False)
+    assert s.max() <= ref.max() + 1e-6
 
 
 # ---------------------------------------------------------------------------
