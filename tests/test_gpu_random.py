@@ -5,7 +5,10 @@ draw shapes (1 to 1500 by 1 to 3000, either orientation, ragged against
 every tile), batch sizes, I/O dtypes, forms, step counts, restart masks and
 forced tile edges from a fixed seed, and check each member against the
 oracle: the relative Frobenius error and the worst 64 x 64 block error,
-with the bars of the coverage tests, and a clear status word.
+with the bars of the coverage tests, and a clear status word.  The
+soft-threshold split runs on sizes from one element to 4096 x 8192 and on
+heavy-tailed, Gaussian, heavily tied and mostly zero inputs, with the median
+and every clip decision compared exactly.
 """
 
 import random
@@ -95,3 +98,53 @@ def test_random_call_matches_oracle(case):
         print(f"  rel err {err:.3e}, worst block {blk:.3e}", flush=True)
         assert err < tol
         assert blk < 2 * tol
+
+
+# ---------------------------------------------------------------------------
+# Soft-threshold split on random sizes and distributions.
+# ---------------------------------------------------------------------------
+
+def _split_cases():
+    rng = random.Random(31)
+    shapes = [(1, 1), (1, 7), (2, 3), (1, 65536), (3, 65537), (777, 1001), (2048, 8192), (4096, 8192)]
+    out = []
+    for i, shape in enumerate(shapes):
+        for dist in ("student_t", "gaussian", "ties", "mostly_zero"):
+            out.append((i, shape, dist, rng.choice(["bf16", "bf16", "fp16", "fp32"])))
+    return out
+
+
+def _split_input(shape, dist, dtype, seed):
+    if dist == "student_t":
+        return workloads.student_t(shape, seed, 2.0, dtype)
+    rng = np.random.default_rng([seed, *shape])
+    if dist == "gaussian":
+        x = rng.standard_normal(shape)
+    elif dist == "ties":
+        x = rng.integers(-3, 4, size=shape).astype(np.float64)
+    else:
+        x = rng.standard_normal(shape) * (rng.random(shape) < 0.05)
+    return workloads.round_to(x.astype(np.float32), dtype)
+
+
+@pytest.mark.parametrize("case", _split_cases(), ids=lambda c: "s%d-%s" % (c[0], c[2]))
+def test_random_split_matches_oracle(case):
+    dev = _dev()
+    i, shape, dist, dtype = case
+    print(f"split {case}", flush=True)
+    m = _split_input(shape, dist, dtype, seed=200 + i)
+    m64 = m.double().numpy()
+    lam_out = torch.zeros(1, dtype=torch.float32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    b, o = nsa.soft_threshold_split(m.to(dev), lambda_out=lam_out, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    lam = lam_out.item()
+    # The lower median of |M| is an order statistic of the stored values;
+    # lambda is 3 x median rounded once to fp32.
+    assert lam == float(np.float32(3.0 * oracle.lower_median_abs(m64)))
+    b_ref, o_ref, _ = oracle.soft_threshold_split(m64, lam=lam)
+    assert np.array_equal(b.double().cpu().numpy(), workloads.round_to(b_ref, dtype).double().numpy())
+    ulp = {"bf16": 2.0 ** -7, "fp16": 2.0 ** -10, "fp32": 2.0 ** -23}[dtype]
+    o = o.double().cpu().numpy()
+    assert np.all(np.abs(o - o_ref) <= ulp * (np.abs(o_ref) + lam))
