@@ -214,8 +214,14 @@ constexpr int kSelWords = kSelFineWords + kSelCopies * kSelGroups;
 template <typename IO>
 __global__ void __launch_bounds__(kSelThreads) k_hist16(const IO* M, int64_t numel, uint32_t* hist, int vec_ok) {
   __shared__ __attribute__((aligned(16))) uint32_t h[kKeyBins16];
-  for (int i = threadIdx.x; i < kKeyBins16 / 4; i += kSelThreads) reinterpret_cast<uint4*>(h)[i] = uint4{0, 0, 0, 0};
-  __syncthreads();
+  // The histogram is cleared after this thread's first load is issued, so
+  // the clearing overlaps that load's latency; the barrier waits for the LDS
+  // stores only (a fenced barrier would also wait for the load).
+  auto clear = [&]() {
+    for (int i = threadIdx.x; i < kKeyBins16 / 4; i += kSelThreads) reinterpret_cast<uint4*>(h)[i] = uint4{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));  // LDS stores only
+    lds_barrier();
+  };
   auto count = [&](uint32_t raw) { atomicAdd(&h[raw & 0x7fffu], 1u); };
   auto count_chunk = [&](const uint4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -228,45 +234,61 @@ __global__ void __launch_bounds__(kSelThreads) k_hist16(const IO* M, int64_t num
   const int64_t tid = (int64_t)blockIdx.x * kSelThreads + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kSelThreads;
   int64_t done = 0;
-  if (vec_ok) {
+  if (vec_ok) {  // uniform: a kernel argument
     const int64_t nvec = numel / 8;
     const uint4* Mv = reinterpret_cast<const uint4*>(M);
+    // Software-pipelined: each 16-byte load is issued before the previous
+    // one is counted, so the LDS atomics overlap the memory latency.
     int64_t i = tid;
-    // Eight 16-byte loads in flight per thread (128 KiB per compute unit):
-    // one round covers 16.7 M 16-bit elements on 256 blocks.
-    for (; i + 7 * stride < nvec; i += 8 * stride) {
-      uint4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = Mv[i + u * stride];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) count_chunk(v[u]);
+    const bool any = i < nvec;
+    uint4 cur = uint4{0, 0, 0, 0};
+    if (any) cur = Mv[i];
+    clear();  // every thread of the block
+    if (any) {
+      for (i += stride; i < nvec; i += stride) {
+        const uint4 nxt = Mv[i];
+        count_chunk(cur);
+        cur = nxt;
+      }
+      count_chunk(cur);
     }
-    for (; i < nvec; i += stride) count_chunk(Mv[i]);
     done = nvec * 8;
+  } else {
+    clear();
   }
   for (int64_t i = done + tid; i < numel; i += stride) count((uint32_t)__builtin_bit_cast(uint16_t, M[i]));
   __syncthreads();
   // Flush: key k * kSelThreads + t for thread t (neighbouring lanes read
-  // neighbouring words, no LDS bank conflicts).  Nonzero bins also go into
-  // an LDS array of group totals, so each group costs one global atomic per
-  // work-group.
-  __shared__ uint32_t gsum[kSelGroups];
-  for (int i = threadIdx.x; i < kSelGroups; i += kSelThreads) gsum[i] = 0u;
-  __syncthreads();
+  // neighbouring words, no LDS bank conflicts); nonzero bins only.  All 32
+  // reads are issued before the first atomic, so their latencies overlap.
   const int copy = blockIdx.x % kSelCopies;
   uint32_t* hg = hist + (int64_t)copy * kKeyBins16;
-  for (int k = 0; k < kKeyBins16 / kSelThreads; ++k) {
-    const int bin = k * kSelThreads + threadIdx.x;
-    const uint32_t c = h[bin];
-    if (c) {
-      atomicAdd(&hg[bin], c);
-      atomicAdd(&gsum[bin / kSelGroup], c);
+  constexpr int kPerThread = kKeyBins16 / kSelThreads;
+  uint32_t c[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) c[k] = h[k * kSelThreads + threadIdx.x];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k)
+    if (c[k]) atomicAdd(&hg[k * kSelThreads + threadIdx.x], c[k]);
+  // Group totals: four neighbouring threads share a group, each adding 32
+  // of its keys (8 16-byte reads, rotated by the lane so that neighbouring
+  // threads, 128 bytes apart, meet fewer banks at once); two quad moves sum
+  // the four, and one thread adds the total into the coarse histogram.
+  static_assert(kSelGroups * 4 == kSelThreads && kSelGroup == 4 * 32, "four threads of 32 keys per group");
+  {
+    const int t = threadIdx.x;
+    const uint4* hv = reinterpret_cast<const uint4*>(h) + t * 8;
+    uint32_t part = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = hv[(j + t) & 7];
+      part += v.x + v.y + v.z + v.w;
     }
+    // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of a quad ends with the sum.
+    part += (uint32_t)__builtin_amdgcn_mov_dpp((int)part, 0xB1, 0xF, 0xF, false);
+    part += (uint32_t)__builtin_amdgcn_mov_dpp((int)part, 0x4E, 0xF, 0xF, false);
+    if ((t & 3) == 0 && part) atomicAdd(&hist[kSelFineWords + copy * kSelGroups + (t >> 2)], part);
   }
-  __syncthreads();
-  uint32_t* coarse = hist + kSelFineWords + copy * kSelGroups;
-  for (int i = threadIdx.x; i < kSelGroups; i += kSelThreads)
-    if (gsum[i]) atomicAdd(&coarse[i], gsum[i]);
 }
 
 // One block: the key holding rank st->rank; lambda = mult * its value.
