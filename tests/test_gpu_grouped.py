@@ -91,3 +91,28 @@ def test_grouped_strided_members_and_ragged_shape(dtype):
         assert torch.equal(single, xs[i]), i
         err = rel_err(xs[i].double().cpu().numpy(), _oracle(mats[i].double().numpy(), "gram"))
         assert err < tol, (i, err)
+
+
+def test_grouped_member_table_in_several_chunks():
+    # More members than one launch's argument block carries (128): the
+    # member table is written by three launches (128 + 128 + 44 entries).
+    # Every member, wide or tall, in its own allocation, must equal the
+    # batched call on the same matrices bit for bit (the tall ones
+    # transposed into the wide orientation first, which is exact).
+    dev = _dev()
+    count = 300
+    wide = [workloads.gaussian((48, 80), seed=900 + i, dtype="bf16") for i in range(count)]
+    xs = [(w.t().contiguous() if i % 5 == 2 else w.clone()).to(dev) for i, w in enumerate(wide)]
+    print(f"grouped table chunks: {count} members", flush=True)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    nsa.orthogonalize_grouped(xs, mode="gram", status=st)
+    stacked = torch.stack(wide).to(dev)
+    nsa.orthogonalize_batched(stacked, mode="gram")
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    for i in range(count):
+        got = xs[i].t() if i % 5 == 2 else xs[i]
+        assert torch.equal(got, stacked[i]), i
+    for i in (0, 127, 128, 257, 299):
+        ref = _oracle(wide[i].double().numpy(), "gram")
+        assert rel_err(stacked[i].double().cpu().numpy(), ref) < 1e-2, i
