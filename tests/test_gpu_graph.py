@@ -6,7 +6,8 @@ captured with torch.cuda.graph and replayed.  Each test captures one call
 with static inputs and workspace, then replays it several times with eager
 calls of the library and synchronizations between the replays, and compares
 every replay with an eager call on the same input: bitwise, with a clear
-status word.
+status word.  Covered: single and batched calls, chained Muon steps, the
+soft-threshold split, a grouped call and the allocation-free entry point.
 """
 
 import pytest
@@ -143,3 +144,53 @@ def test_soft_threshold_split_replays_equal_eager():
         b2, _ = nsa.soft_threshold_split(m0.clone())
         torch.cuda.synchronize()
         assert torch.equal(b2, b_ref), i
+
+
+def test_grouped_call_replays_equal_eager():
+    # The member table goes to the device as a kernel argument, so a
+    # captured grouped call replays with the members it was captured with.
+    dev = _dev()
+    mats = [workloads.gaussian((96, 320), seed=60 + i, dtype="bf16") for i in range(5)]
+    host = [m.t().contiguous() if i % 2 else m for i, m in enumerate(mats)]
+    ref = [h.to(dev) for h in host]
+    nsa.orthogonalize_grouped(ref, mode="gram")
+    torch.cuda.synchronize()
+    xs = [h.to(dev) for h in host]
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    need = nsa.grouped_workspace_size(96, 320, len(xs), torch.bfloat16, "gram")
+    ws = _ws(need, dev)
+    g = _capture(lambda: nsa.orthogonalize_grouped(xs, mode="gram", workspace=ws, status=st))
+    for i in range(REPLAYS):
+        for x, h in zip(xs, host):
+            x.copy_(h.to(dev))
+        st.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, i
+        for j, (x, r) in enumerate(zip(xs, ref)):
+            assert torch.equal(x, r), (i, j)
+        other = [h.to(dev) for h in host]
+        nsa.orthogonalize_grouped(other, mode="gram")
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, r) for o, r in zip(other, ref)), i
+
+
+def test_static_call_replays_equal_eager():
+    # The allocation-free entry point works in the library's own device
+    # scratch; eager calls between the replays use the same scratch.
+    dev = _dev()
+    x0 = workloads.column_scaled(512, 1536, seed=61, dtype="bf16").to(dev)
+    ref = x0.clone()
+    nsa.orthogonalize_static(ref, mode="gram")
+    torch.cuda.synchronize()
+    xs = x0.clone()
+    g = _capture(lambda: nsa.orthogonalize_static(xs, mode="gram"))
+    for i in range(REPLAYS):
+        xs.copy_(x0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xs, ref), i
+        other = x0.clone()
+        nsa.orthogonalize_static(other, mode="gram")
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref), i
