@@ -377,7 +377,10 @@ ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch,
  * LDS, Eg when it is read from global memory and noE when there is none.
  * A trailing ",nt" marks the pair/pairloop builds whose output stores are
  * non-temporal, taken by a launch that writes more than 256 MiB (the
- * MI355X MALL's size) and reads no guard flags or member table.  The list
+ * MI355X MALL's size) and reads no guard flags or member table.  A ",x"
+ * before it marks the builds that read such extended arguments: every
+ * launch of a guarded Gram call (opt->guard_threshold > 0) except the
+ * first step's n x n product, and a grouped call's final product.  The list
  * follows the call's launches by kind: the norm and staging passes, the
  * X X^T builds, the n x n builds, the intermediate updates, the final
  * product.
@@ -385,6 +388,15 @@ ns_status ns_muon_step(void* W, const void* G, float* M, int64_t batch,
 int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch,
                         ns_dtype dtype, ns_mode mode, int32_t steps,
                         const ns_options* opt, char* buf, size_t len);
+
+/*
+ * The same list for a grouped call (ns_orthogonalize_grouped) of `count`
+ * matrices of shape n x m up to orientation (n <= m; -1 otherwise).  For
+ * inspection only, like ns_plan_kernels.
+ */
+int64_t ns_plan_kernels_grouped(int64_t n, int64_t m, int64_t count,
+                                ns_dtype dtype, ns_mode mode, int32_t steps,
+                                const ns_options* opt, char* buf, size_t len);
 
 /* Static description of a status code. */
 const char* ns_status_string(ns_status s);

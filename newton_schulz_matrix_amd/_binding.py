@@ -123,6 +123,11 @@ _SIGNATURES = {
                          ctypes.c_int, ctypes.c_int, ctypes.c_int32,
                          ctypes.POINTER(Options), ctypes.c_char_p,
                          ctypes.c_size_t]),
+    "ns_plan_kernels_grouped": (ctypes.c_int64,
+                                [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int32,
+                                 ctypes.POINTER(Options), ctypes.c_char_p,
+                                 ctypes.c_size_t]),
     "ns_muon_workspace_size": (ctypes.c_size_t,
                                [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                 ctypes.c_int, ctypes.c_int,
@@ -281,18 +286,25 @@ def workspace_size(rows: int, cols: int, batch: int = 1,
 def plan_kernels(rows: int, cols: int, batch: int = 1,
                  dtype: torch.dtype = torch.bfloat16, mode: str = "standard",
                  steps: int = 5, restart_mask: int = 1 << 4,
-                 internal: Optional[str] = None, tile: int = 0) -> List[str]:
-    """The kernel builds one call would launch (host only, no device)."""
-    opt = make_options(restart_mask, 1e-7, internal, tile=tile)
-    need = int(lib().ns_plan_kernels(rows, cols, batch, dtype_code(dtype),
-                                     _MODE_CODE[mode], steps,
-                                     ctypes.byref(opt), None, 0))
+                 internal: Optional[str] = None, tile: int = 0,
+                 guard: float = 0.0, grouped: bool = False) -> List[str]:
+    """The kernel builds one call would launch (host only, no device).
+
+    ``grouped``: a grouped call of ``batch`` matrices of this shape up to
+    orientation (orthogonalize_grouped) instead of a batched one."""
+    opt = make_options(restart_mask, 1e-7, internal, tile=tile, guard=guard)
+    if grouped:
+        fn, args = lib().ns_plan_kernels_grouped, (min(rows, cols), max(rows, cols))
+    else:
+        fn, args = lib().ns_plan_kernels, (rows, cols)
+    name = "ns_plan_kernels_grouped" if grouped else "ns_plan_kernels"
+    need = int(fn(*args, batch, dtype_code(dtype), _MODE_CODE[mode], steps,
+                  ctypes.byref(opt), None, 0))
     if need < 0:
-        raise NSError(1, "ns_plan_kernels")
+        raise NSError(1, name)
     buf = ctypes.create_string_buffer(need)
-    lib().ns_plan_kernels(rows, cols, batch, dtype_code(dtype),
-                          _MODE_CODE[mode], steps, ctypes.byref(opt), buf,
-                          need)
+    fn(*args, batch, dtype_code(dtype), _MODE_CODE[mode], steps,
+       ctypes.byref(opt), buf, need)
     return buf.value.decode().split()
 
 

@@ -320,18 +320,37 @@ ns_status ns_orthogonalize_batched(void* X, int64_t batch, int64_t rows, int64_t
                             workspace_bytes, stream);
 }
 
-int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode, int32_t steps,
-                        const ns_options* opt, char* buf, size_t len) {
+}  // extern "C"
+
+namespace {
+
+int64_t plan_string(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode, int32_t steps,
+                    const ns_options* opt, bool grouped, char* buf, size_t len) {
   Plan p;
   if (make_plan(rows, cols, batch, dtype, mode, opt, &p) != NS_OK || steps < 1 || steps > NS_MAX_STEPS) return -1;
   const std::string d =
-      describe_plan(p, steps, opt ? opt->restart_mask : (1u << 4), opt && opt->guard_threshold > 0.f);
+      describe_plan(p, steps, opt ? opt->restart_mask : (1u << 4), opt && opt->guard_threshold > 0.f, grouped);
   if (buf && len > 0) {
     const size_t n = std::min(len - 1, d.size());
     memcpy(buf, d.data(), n);
     buf[n] = 0;
   }
   return (int64_t)d.size() + 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ns_plan_kernels(int64_t rows, int64_t cols, int64_t batch, ns_dtype dtype, ns_mode mode, int32_t steps,
+                        const ns_options* opt, char* buf, size_t len) {
+  return plan_string(rows, cols, batch, dtype, mode, steps, opt, false, buf, len);
+}
+
+int64_t ns_plan_kernels_grouped(int64_t n, int64_t m, int64_t count, ns_dtype dtype, ns_mode mode, int32_t steps,
+                                const ns_options* opt, char* buf, size_t len) {
+  if (n > m) return -1;
+  return plan_string(n, m, count, dtype, mode, steps, opt, true, buf, len);
 }
 
 // A grouped call's member table reaches the device through kernel

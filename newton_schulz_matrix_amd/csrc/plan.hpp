@@ -781,7 +781,7 @@ inline const char* form_name(Form f) {
 }
 inline const char* dtype_name(ns_dtype d) { return d == NS_FP32 ? "f32" : d == NS_FP16 ? "f16" : "bf16"; }
 
-inline std::string describe_plan(const Plan& p, int steps, uint32_t mask, bool guard) {
+inline std::string describe_plan(const Plan& p, int steps, uint32_t mask, bool guard, bool grouped) {
   const int esz = p.esz;
   const int64_t per_k = kRowBytes / esz;
   const int64_t km = round_up(p.m, per_k) / per_k, kn = round_up(p.n, per_k) / per_k;
@@ -803,15 +803,22 @@ inline std::string describe_plan(const Plan& p, int steps, uint32_t mask, bool g
     return (f == Form::kPairLoop || f == Form::kPairTile) && !ext && stream_out(bytes) ? std::string(",nt")
                                                                                        : std::string();
   };
-  auto xxt = [&](bool ext) { return "xxt<" + T + "," + E + "," + form_name(fx) + ntag(fx, ext, nn_bytes) + ">"; };
+  // ",x": the build that reads extended arguments (the guard's device flags,
+  // a grouped call's member table); see launch_sym and launch_nt.
+  auto xtag = [](bool ext) { return ext ? std::string(",x") : std::string(); };
+  auto xxt = [&](bool ext) {
+    return "xxt<" + T + "," + E + "," + form_name(fx) + xtag(ext) + ntag(fx, ext, nn_bytes) + ">";
+  };
   auto nn = [&](bool ext, bool c2) {
-    return "nn<" + T + "," + E + "," + form_name(fn) + ntag(fn, ext, nn_bytes * (c2 ? 2.0 : 1.0)) + ">";
+    return "nn<" + T + "," + E + "," + form_name(fn) + xtag(ext) + ntag(fn, ext, nn_bytes * (c2 ? 2.0 : 1.0)) + ">";
   };
   auto upd = [&](bool ext, const std::string& et) {
-    return "upd<" + T + "," + T + "," + E + "," + form_name(fu) + et + ntag(fu, ext, x2_bytes) + ">";
+    return "upd<" + T + "," + T + "," + E + "," + form_name(fu) + et + xtag(ext) + ntag(fu, ext, x2_bytes) + ">";
   };
+  // A grouped call's final product reads the member table.
   auto fin = [&](bool ext, const std::string& et) {
-    return "out<" + T + "," + IO + "," + E + "," + form_name(fu) + et + ntag(fu, ext, out_bytes) + ">";
+    ext = ext || grouped;
+    return "out<" + T + "," + IO + "," + E + "," + form_name(fu) + et + xtag(ext) + ntag(fu, ext, out_bytes) + ">";
   };
   // The launches of one call, in the order of the runner (Runner::run and
   // Runner::run_guarded), by kind.

@@ -35,7 +35,8 @@ def test_header_declares_the_api():
                  "ns_muon_step", "ns_muon_workspace_size",
                  "ns_soft_threshold_split", "ns_workspace_size",
                  "ns_soft_threshold_workspace_size", "ns_status_string",
-                 "ns_options_default", "ns_version", "ns_plan_kernels"]:
+                 "ns_options_default", "ns_version", "ns_plan_kernels",
+                 "ns_plan_kernels_grouped"]:
         assert want in names
 
 
@@ -305,7 +306,7 @@ def test_guard_threshold_checks():
     opt = B.make_options(restart_mask=0, guard=100.0)
     buf = ctypes.create_string_buffer(512)
     B.lib().ns_plan_kernels(300, 700, 1, B.NS_BF16, B.NS_GRAM, 5, ctypes.byref(opt), buf, 512)
-    assert "upd<f16,f16,128,tile,noE>" in buf.value.decode().split()
+    assert "upd<f16,f16,128,tile,noE,x>" in buf.value.decode().split()
 
 
 def test_plan_kernels_names_the_builds():
@@ -332,6 +333,22 @@ def test_plan_kernels_names_the_builds():
     ks = nsa.plan_kernels(300, 200, 1, torch.float32, "standard")
     assert "upd<f32,f32,64,tile,Eg>" in ks
     assert B.lib().ns_plan_kernels(0, 5, 1, 0, 0, 5, None, None, 0) == -1
+    # Builds that read extended arguments carry ",x": with the guard every
+    # launch but the first step's n x n product (and never the non-temporal
+    # builds); in a grouped call the final product only.
+    ks = nsa.plan_kernels(4096, 14336, 1, torch.bfloat16, "gram", guard=100.0)
+    assert ks == ["sumsq<bf16>", "stage<bf16,f16>", "xxt<f16,192,tile,x>",
+                  "nn<f16,192,tile>", "nn<f16,192,tile,x>",
+                  "upd<f16,f16,192,tile,noE,x>", "out<f16,bf16,192,tile,noE,x>"]
+    ks = nsa.plan_kernels(2048, 1408, 128, torch.bfloat16, "gram", guard=100.0)
+    assert ks[2:4] == ["xxt<f16,128,pairloop,x>", "nn<f16,128,pairloop,nt>"]
+    for orient in ((768, 3072), (3072, 768)):
+        ks = nsa.plan_kernels(*orient, 24, torch.bfloat16, "standard", grouped=True)
+        assert ks[2:] == ["xxt<f16,192,tile>", "nn<f16,192,tile>",
+                          "upd<f16,f16,192,loop,E>", "out<f16,bf16,192,loop,E,x>"]
+    opt = B.make_options()
+    assert B.lib().ns_plan_kernels_grouped(3072, 768, 24, B.NS_BF16, B.NS_GRAM, 5,
+                                           ctypes.byref(opt), None, 0) == -1
 
 
 def test_batched_argument_checks():

@@ -10,7 +10,10 @@ iteration on the host the worst block runs 1.2 to 1.5 times the global
 error, while a wrong tile gives errors of the order of the entries).  The
 batched calls carry a status word, which must stay clear, and sampled
 members must equal single calls (other kernel builds, no status word) bit
-for bit.
+for bit.  The builds that read extended arguments run too: each case
+guarded (equal to the fixed schedule bit for bit at a threshold no
+statistic reaches) and as a grouped call (equal to the plain call bit for
+bit).
 """
 
 import numpy as np
@@ -79,3 +82,53 @@ def test_every_build_matches_oracle(case, mode):
             nsa.orthogonalize(single, mode=mode, tile=tile)
             torch.cuda.synchronize()
             assert torch.equal(single, got), i
+
+
+def _plain(m, dev, mode, tile):
+    x = m.to(dev)
+    fn = nsa.orthogonalize if m.dim() == 2 else nsa.orthogonalize_batched
+    fn(x, mode=mode, tile=tile)
+    return x
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_every_guarded_build_equals_fixed_schedule(case):
+    # The guard's builds (extended arguments: device flags) at a threshold
+    # no statistic reaches: the fixed schedule (restart before step 4) bit
+    # for bit, with a clear status word.  The fixed schedule itself is
+    # checked against the oracle above.
+    dev = _dev()
+    batch, rows, cols, dtype, tile = case
+    print(f"guarded {case}", flush=True)
+    m = _input(batch, rows, cols, dtype, seed=rows + cols + batch)
+    fixed = _plain(m, dev, "gram", tile)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    x = m.to(dev)
+    fn = nsa.orthogonalize if batch == 1 else nsa.orthogonalize_batched
+    fn(x, mode="gram", tile=tile, guard=1e30, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    assert torch.equal(x, fixed)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_every_grouped_build_equals_plain_call(case, mode):
+    # The same matrices as a grouped call (each in its own allocation; the
+    # final product reads the member table): equal to the batched or single
+    # call bit for bit, with a clear status word.
+    dev = _dev()
+    batch, rows, cols, dtype, tile = case
+    print(f"grouped {case} {mode}", flush=True)
+    m = _input(batch, rows, cols, dtype, seed=rows + cols + batch)
+    plain = _plain(m, dev, mode, tile)
+    members = [m.to(dev)] if batch == 1 else [m[i].to(dev) for i in range(batch)]
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    nsa.orthogonalize_grouped(members, mode=mode, tile=tile, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    if batch == 1:
+        assert torch.equal(members[0], plain)
+    else:
+        for i in range(batch):
+            assert torch.equal(members[i], plain[i]), i
