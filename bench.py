@@ -24,7 +24,10 @@ Prints one JSON line.  Besides the driver's fields it carries:
   standard_form          the same measurement for the standard form;
   roofline               the dominant kernel's achieved rate (HIP events
                          bound to each launch, in an instrumented run of the
-                         same number of steps right after the timed region);
+                         same number of steps right after the timed region),
+                         on algorithmic FLOPs; issued_tflops / issued_frac
+                         count the MFMA work the launches actually issue
+                         (whole diagonal tiles, padded edges) instead;
   kernels                per-kernel-kind average launch times (the
                          instrumented run);
   ms_per_step_instrumented, ms_p10_p50_p90
@@ -386,6 +389,22 @@ def committed_traffic(kind, workload, mode, tile):
     return None, None
 
 
+def issued_flops(kind, batch, rows, cols, tile, internal):
+    """MFMA work one launch of a symmetric product actually issues: whole
+    upper-triangle tiles of `tile` (diagonal tiles in full, ragged edges
+    padded) over the contraction rounded up to the k-tile.  kind "sym" is an
+    n x n product (contraction n), "gram" X X^T (contraction m); None for
+    other kinds."""
+    if kind not in ("sym", "gram"):
+        return None
+    n, m = min(rows, cols), max(rows, cols)
+    kt = 32 if internal == "fp32" else 64          # elements per 128-byte k-tile row
+    k = n if kind == "sym" else m
+    k_pad = -(-k // kt) * kt
+    t = -(-n // tile)
+    return batch * (t * (t + 1) // 2) * tile * tile * k_pad * 2.0
+
+
 def cpu_baseline(m_cpu, mode, restart_mask):
     import numpy as np
     import oracle
@@ -544,6 +563,19 @@ def main():
     roof["kernel"] = dom
     roof["avg_launch_ms"] = avg_ms
     roof["launches_timed"] = ks["launches"]
+    # Supplementary: the same launches counted by the MFMA work they issue
+    # (whole diagonal tiles, padded edges), which separates the kernel's own
+    # rate from the tile geometry's overhead.  Single-call steps only.
+    if len(shapes) == 1 and not any(isinstance(m, list) for m in host_inputs):
+        b, r, c = shapes[0]
+        plan = nsa.plan_kernels(r, c, b, {"bf16": torch.bfloat16, "fp16": torch.float16,
+                                          "fp32": torch.float32}[io], args.mode,
+                                5, args.restart_mask, args.internal, args.tile)
+        edge = [int(k.split(",")[1]) for k in plan if k.startswith("nn<")]
+        issued = issued_flops(dom, b, r, c, edge[0], internal) if edge else None
+        if issued:
+            roof["issued_tflops"] = issued / (avg_ms * 1e-3) / 1e12
+            roof["issued_frac"] = roof["issued_tflops"] / roof["peak"]
 
     kernels = {}
     for k, s in res["timed_kernels"].items():

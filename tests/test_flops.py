@@ -65,3 +65,26 @@ def test_counter_by_enumeration():
     assert gram_flops(n, m, t, (3,)) == expect
     assert ns_flops(m, n, t, "gram", 1 << 3) == expect
     assert ns_flops(n, m, t, "standard") == t * (sym_nm + sym_nn + dense_nm)
+
+
+def test_bench_issued_work_counts_whole_tiles():
+    # The bench's supplementary roofline counts the MFMA work a symmetric
+    # launch issues: every upper-triangle tile in full, contraction rounded
+    # up to the k-tile (64 elements for 16-bit operands, 32 for fp32).
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    # 4096 on 192 tiles: 22 blocks (the last 64 wide), 253 tiles.
+    assert bench.issued_flops("sym", 1, 4096, 14336, 192, "fp16") == 253 * 192 ** 2 * 4096 * 2
+    assert bench.issued_flops("gram", 1, 14336, 4096, 192, "fp16") == 253 * 192 ** 2 * 14336 * 2
+    # 2048 on 128 tiles: 136 tiles; the expert batch: 66 tiles per matrix.
+    assert bench.issued_flops("sym", 1, 2048, 8192, 128, "fp16") == 136 * 128 ** 2 * 2048 * 2
+    assert bench.issued_flops("sym", 128, 2048, 1408, 128, "fp16") == 128 * 66 * 128 ** 2 * 1408 * 2
+    # fp32: 256 on 64 tiles, contraction in 32-element k-tiles; ragged n.
+    assert bench.issued_flops("sym", 1, 256, 1024, 64, "fp32") == 10 * 64 ** 2 * 256 * 2
+    assert bench.issued_flops("sym", 1, 100, 300, 64, "fp32") == 3 * 64 ** 2 * 128 * 2
+    # Symmetric products only; the issued count is never below the
+    # algorithmic one (n^3 for an n x n product).
+    assert bench.issued_flops("update", 1, 4096, 14336, 192, "fp16") is None
+    for n in (1, 100, 1000, 4096):
+        assert bench.issued_flops("sym", 1, n, 2 * n, 128, "fp16") >= n ** 3
