@@ -187,3 +187,30 @@ def test_matrix_above_2gib_block_embedding(tall):
     assert err < 1e-2
     x[r0:r0 + br, c0:c0 + bc] = 0
     assert torch.count_nonzero(x).item() == 0
+
+
+@pytest.mark.parametrize("mode", ["gram", "standard"])
+def test_largest_batch(mode):
+    # 65535 members, the largest batch a call takes (one grid dimension of
+    # the per-matrix kernels): 17 x 40 bf16 Gaussian matrices, one 128 tile
+    # each, so every product launch has 65535 tiles (two work-groups per
+    # CU, persistent, non-temporal stores).  Sampled members, first and last
+    # included, equal single calls bit for bit and the oracle within the bar.
+    dev = _dev()
+    batch = 65535
+    m = workloads.gaussian((batch, 17, 40), seed=95, dtype="bf16")
+    print(f"largest batch: {batch} x 17 x 40 {mode}", flush=True)
+    x = m.to(dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    nsa.orthogonalize_batched(x, mode=mode, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    for i in (0, 1, 4096, 32767, batch - 2, batch - 1):
+        single = m[i].to(dev)
+        nsa.orthogonalize(single, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(single, x[i]), i
+        err = _rel(x[i].double().cpu().numpy(), _oracle(m[i].double().numpy(), mode))
+        assert err < 1e-2, (i, err)
+    del x
+    torch.cuda.empty_cache()
