@@ -214,3 +214,54 @@ def test_largest_batch(mode):
         assert err < 1e-2, (i, err)
     del x
     torch.cuda.empty_cache()
+
+
+def test_split_past_2_31_elements_closed_form():
+    # 2^31 + 13 bf16 elements (4 GiB) of a periodic pattern whose lower
+    # median of |M| follows from counting one period: v_i = (i mod 7) - 3,
+    # times 101 where i mod 1000 == 0 (the outliers).  lambda = 3 x median
+    # (in fp32), B = clip(M, -lambda, lambda) and O = M - B then follow
+    # elementwise.  Runs the select and the split with indices past 2^31.
+    dev = _dev()
+    numel = (1 << 31) + 13
+    period = 7000
+    print(f"split of {numel} elements", flush=True)
+
+    def value(i):
+        v = (i % 7) - 3
+        return v * 101 if i % 1000 == 0 else v
+
+    counts = {}
+    full, rest = divmod(numel, period)
+    for i in range(period):
+        a = abs(value(i))
+        counts[a] = counts.get(a, 0) + full + (1 if i < rest else 0)
+    assert sum(counts.values()) == numel
+    want, acc = (numel + 1) // 2, 0
+    for a in sorted(counts):
+        acc += counts[a]
+        if acc >= want:
+            median = a
+            break
+    lam = float(torch.tensor(3.0 * median, dtype=torch.float32))
+    chunk = 1 << 28
+    m = torch.empty(numel, dtype=torch.bfloat16, device=dev)
+    for s in range(0, numel, chunk):
+        idx = torch.arange(s, min(s + chunk, numel), device=dev, dtype=torch.int64)
+        m[s:s + idx.numel()] = ((idx % 7 - 3) * torch.where(idx % 1000 == 0, 101, 1)).to(torch.bfloat16)
+    del idx
+    lam_out = torch.zeros(1, dtype=torch.float32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    b, o = nsa.soft_threshold_split(m, lambda_out=lam_out, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    assert lam_out.item() == lam
+    nonzero_o = 0
+    for s in range(0, numel, chunk):
+        ms, bs, os_ = m[s:s + chunk], b[s:s + chunk], o[s:s + chunk]
+        assert torch.equal(bs, ms.clamp(-lam, lam)), s
+        assert torch.equal(os_, (ms.float() - bs.float()).to(torch.bfloat16)), s
+        nonzero_o += int(torch.count_nonzero(os_).item())
+    assert nonzero_o == sum(c for a, c in counts.items() if a > lam)
+    del m, b, o
+    torch.cuda.empty_cache()
