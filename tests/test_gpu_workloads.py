@@ -216,16 +216,18 @@ def test_largest_batch(mode):
     torch.cuda.empty_cache()
 
 
-def test_split_past_2_31_elements_closed_form():
-    # 2^31 + 13 bf16 elements (4 GiB) of a periodic pattern whose lower
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_split_past_2_31_elements_closed_form(dtype):
+    # 2^31 + 13 elements (4 or 8 GiB) of a periodic pattern whose lower
     # median of |M| follows from counting one period: v_i = (i mod 7) - 3,
     # times 101 where i mod 1000 == 0 (the outliers).  lambda = 3 x median
     # (in fp32), B = clip(M, -lambda, lambda) and O = M - B then follow
-    # elementwise.  Runs the select and the split with indices past 2^31.
+    # elementwise.  Runs the select (one pass over 16-bit keys, three radix
+    # passes for fp32) and the split with indices past 2^31.
     dev = _dev()
     numel = (1 << 31) + 13
     period = 7000
-    print(f"split of {numel} elements", flush=True)
+    print(f"split of {numel} elements, {dtype}", flush=True)
 
     def value(i):
         v = (i % 7) - 3
@@ -245,10 +247,10 @@ def test_split_past_2_31_elements_closed_form():
             break
     lam = float(torch.tensor(3.0 * median, dtype=torch.float32))
     chunk = 1 << 28
-    m = torch.empty(numel, dtype=torch.bfloat16, device=dev)
+    m = torch.empty(numel, dtype=dtype, device=dev)
     for s in range(0, numel, chunk):
         idx = torch.arange(s, min(s + chunk, numel), device=dev, dtype=torch.int64)
-        m[s:s + idx.numel()] = ((idx % 7 - 3) * torch.where(idx % 1000 == 0, 101, 1)).to(torch.bfloat16)
+        m[s:s + idx.numel()] = ((idx % 7 - 3) * torch.where(idx % 1000 == 0, 101, 1)).to(dtype)
     del idx
     lam_out = torch.zeros(1, dtype=torch.float32, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -260,7 +262,7 @@ def test_split_past_2_31_elements_closed_form():
     for s in range(0, numel, chunk):
         ms, bs, os_ = m[s:s + chunk], b[s:s + chunk], o[s:s + chunk]
         assert torch.equal(bs, ms.clamp(-lam, lam)), s
-        assert torch.equal(os_, (ms.float() - bs.float()).to(torch.bfloat16)), s
+        assert torch.equal(os_, (ms.float() - bs.float()).to(dtype)), s
         nonzero_o += int(torch.count_nonzero(os_).item())
     assert nonzero_o == sum(c for a, c in counts.items() if a > lam)
     del m, b, o
