@@ -381,3 +381,58 @@ def test_soft_threshold_unaligned_and_ragged(dtype):
     b_n, o_n = nsa.soft_threshold_split(aligned.clone(), outliers=False)
     torch.cuda.synchronize()
     assert o_n is None and torch.equal(b_n, b_a)
+
+
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+@pytest.mark.parametrize("tall", [False, True])
+def test_zero_rows_and_columns_stay_exactly_zero(mode, tall):
+    # Rank-deficient by construction: zero rows and columns of X give zero
+    # rows and columns of X X^T and of every n x n matrix built from it, so
+    # the result keeps them exactly zero (p(0) = 0 needs no special case).
+    # The rest is the orthogonalization of the nonzero submatrix.
+    dev = _dev()
+    m = workloads.gaussian((300, 700), seed=71, dtype="bf16").clone()
+    zr, zc = [5, 77, 299], [0, 350, 699]
+    m[zr, :] = 0
+    m[:, zc] = 0
+    if tall:
+        m = m.t().contiguous()
+    x = m.to(dev)
+    nsa.orthogonalize(x, mode=mode)
+    torch.cuda.synchronize()
+    out = x.t() if tall else x
+    assert torch.count_nonzero(out[zr, :]).item() == 0
+    assert torch.count_nonzero(out[:, zc]).item() == 0
+    ref = _oracle(m.double().numpy(), mode)
+    assert _rel(x.double().cpu().numpy(), ref) < 1e-2
+
+
+@pytest.mark.parametrize("mode", ["standard", "gram"])
+@pytest.mark.parametrize("rank", [8, 40])
+def test_low_rank_input_signal_and_null_parts(mode, rank):
+    # M = A B^T of rank r, rounded to bf16.  On M's top-r right singular
+    # subspace the result matches the oracle within the 1e-2 bar.  Off it,
+    # both results hold only rounding noise that the iteration amplifies (up
+    # to the product of the a_k, about 486, near zero): the oracle's from the
+    # bf16 input, the device's from that plus its fp16 state, whose unit
+    # roundoff (2^-11) is a quarter of bf16's (2^-9).  So the difference off
+    # the subspace stays below half the oracle's own part there.
+    dev = _dev()
+    rng = np.random.default_rng(72 + rank)
+    a, b = rng.standard_normal((300, rank)), rng.standard_normal((700, rank))
+    m = workloads.round_to((a @ b.T).astype(np.float32), "bf16")
+    m64 = m.double().numpy()
+    x = m.to(dev)
+    nsa.orthogonalize(x, mode=mode)
+    torch.cuda.synchronize()
+    out = x.double().cpu().numpy()
+    ref = _oracle(m64, mode)
+    vt = np.linalg.svd(m64, full_matrices=False)[2][:rank]
+    sig = lambda y: y @ vt.T @ vt
+    e_sig = np.linalg.norm(sig(out - ref)) / np.linalg.norm(sig(ref))
+    null_err = np.linalg.norm((out - ref) - sig(out - ref))
+    null_ref = np.linalg.norm(ref - sig(ref))
+    print(f"rank {rank} {mode}: signal rel err {e_sig:.3e}, off-subspace "
+          f"difference {null_err:.3e} against the oracle's {null_ref:.3e}")
+    assert e_sig < 1e-2
+    assert null_err < 0.5 * null_ref
