@@ -5,8 +5,8 @@
 //
 //   sym  : C = beta*E + gamma * L R^T   (L, R: n x K, C, E: n x n)
 //          with a symmetric result, so only tiles (tm <= tn) are computed and
-//          each is also stored mirrored.  X X^T, A A (A symmetric), Z' Q,
-//          Z' R and Z' V are all of this shape (Q, R, V, Z' are polynomials
+//          each is also stored mirrored.  X X^T, A A (A symmetric), Q Z',
+//          R Z' and V Z' are all of this shape (Q, R, V, Z' are polynomials
 //          in the same Gram matrix, so they are symmetric and commute).
 //   nt   : Y = alpha*E + gamma * B X = alpha*E + gamma * B (X^T)^T
 //          (B: n x n, X^T: m x n), the update X <- a X + B X and the Gram
@@ -16,7 +16,8 @@
 //
 // Tile engine (gfx950, CDNA4):
 //   * 256 threads = 4 wave64s in a 2 x 2 grid; square block tiles of 128,
-//     192 or 256 (the same edge for both products of a call); each wave owns
+//     192 or 256 for 16-bit operands, 64 or 128 for fp32 (the same edge for
+//     every product of a call); each wave owns
 //     a (TM/2) x (TN/2) sub-tile made of 32 x 32 MFMA tiles
 //     (v_mfma_f32_32x32x16_f16; for fp32 operands four
 //     v_mfma_f32_32x32x2_f32 per 16-byte chunk).  16-bit input of either
