@@ -1,5 +1,8 @@
-// stage.hpp - HBM-bound passes before the products: the Frobenius norm and
-// the fused scale / cast / orient-to-wide / zero-pad pass.
+// stage.hpp - the small kernels around the products: the Frobenius norm
+// and the fused scale / cast / orient-to-wide / zero-pad pass (both
+// HBM-bound), the non-finite scan of a result (status word), the guarded
+// Gram iteration's flag kernels and restart detector, and the Muon step's
+// momentum pass.
 //
 // The iteration wants X with no more rows than columns (the Gram-NS
 // article's X in R^{n x m}, aspect alpha = m/n) and unit Frobenius norm.
