@@ -436,15 +436,21 @@ def cpu_baseline(m_cpu, mode, restart_mask):
 
 
 def cpu_model():
-    """The host CPU's model name from /proc/cpuinfo."""
+    """The host CPU's model name from /proc/cpuinfo, with its family, model
+    and stepping numbers (a virtualized host may report a generic name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                      # the first processor only
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def root_quality(host_input, mode, args):
