@@ -232,7 +232,7 @@ ns_status threshold_typed(const void* M, void* B, void* O, int64_t numel, float 
     const int64_t want = (numel + (int64_t)kSelThreads * 64 - 1) / ((int64_t)kSelThreads * 64);
     const unsigned g = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 256));
     hipLaunchKernelGGL((k_hist16<IO>), dim3(g), dim3(kSelThreads), 0, st, m, numel, hist, vec_hist);
-    hipLaunchKernelGGL((k_pick16<IO>), dim3(1), dim3(kSelThreads), 0, st, state, hist, mult, d_lambda_out);
+    hipLaunchKernelGGL((k_pick16<IO>), dim3(1), dim3(kPickThreads), 0, st, state, hist, mult, d_lambda_out);
   } else {
     constexpr int kb = KeyOf<IO>::kBits;
     // Digits from the top, at most 11 bits each.

@@ -292,31 +292,43 @@ __global__ void __launch_bounds__(kSelThreads) k_hist16(const IO* M, int64_t num
 }
 
 // One block: the key holding rank st->rank; lambda = mult * its value.
+// 256 threads: thread t holds coarse group t, then key g*128 + t of the
+// chosen group g; both prefix sums are wave scans plus the totals of the
+// waves before.
+constexpr int kPickThreads = 256;
+static_assert(kSelGroups == kPickThreads && kSelGroup <= kPickThreads, "one thread per group and per key");
+
+// Inclusive prefix sum of v over the block's kPickThreads threads.
+__device__ __forceinline__ uint64_t pick_scan(uint64_t v, uint64_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t u = __shfl_up((unsigned long long)v, off, 64);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  __syncthreads();  // wsum is reused by the next scan
+  return v + before;
+}
+
 template <typename IO>
-__global__ void __launch_bounds__(kSelThreads) k_pick16(SelectState* st, const uint32_t* hist, float mult,
-                                                       float* d_lambda_out) {
-  __shared__ uint64_t part[kSelThreads];
+__global__ void __launch_bounds__(kPickThreads) k_pick16(SelectState* st, const uint32_t* hist, float mult,
+                                                        float* d_lambda_out) {
+  __shared__ uint64_t wsum[kPickThreads / 64];
   __shared__ int sh_group;
   __shared__ uint64_t sh_before;
   const uint64_t want = st->rank;
   const int t = threadIdx.x;
-  // Coarse pass: thread t < 256 holds group t's total over the copies.
+  // Coarse pass: group t's total over the copies.
   uint64_t s = 0;
-  if (t < kSelGroups) {
 #pragma unroll
-    for (int k = 0; k < kSelCopies; ++k) s += hist[kSelFineWords + k * kSelGroups + t];
-  }
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const uint64_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
+  for (int k = 0; k < kSelCopies; ++k) s += hist[kSelFineWords + k * kSelGroups + t];
   {
-    const uint64_t incl = part[t], excl = incl - s;
-    if (t < kSelGroups && ((excl < want && want <= incl) || (t == kSelGroups - 1 && want > incl))) {
+    const uint64_t incl = pick_scan(s, wsum), excl = incl - s;
+    if ((excl < want && want <= incl) || (t == kSelGroups - 1 && want > incl)) {
       sh_group = t;
       sh_before = excl;
     }
@@ -330,16 +342,7 @@ __global__ void __launch_bounds__(kSelThreads) k_pick16(SelectState* st, const u
 #pragma unroll
     for (int k = 0; k < kSelCopies; ++k) c += hist[(int64_t)k * kKeyBins16 + g * kSelGroup + t];
   }
-  __syncthreads();
-  part[t] = c;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const uint64_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  const uint64_t incl = before + part[t], excl = incl - c;
+  const uint64_t incl = before + pick_scan(c, wsum), excl = incl - c;
   if (t < kSelGroup && ((excl < want && want <= incl) || (t == kSelGroup - 1 && want > incl))) {
     const uint32_t key = (uint32_t)(g * kSelGroup + t);
     st->rank = want - excl;
