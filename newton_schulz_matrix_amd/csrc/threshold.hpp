@@ -80,6 +80,25 @@ __device__ __forceinline__ uint32_t chunk_bits(const uint4& v, int j) {
     return w[j];
 }
 
+// Inclusive prefix sum of v over a block of kPickThreads threads (four
+// waves): a shuffle scan within each wave plus the totals of the waves
+// before it, two barriers in all.  wsum: kPickThreads / 64 words of LDS.
+constexpr int kPickThreads = 256;
+__device__ __forceinline__ uint64_t pick_scan(uint64_t v, uint64_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t u = __shfl_up((unsigned long long)v, off, 64);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  __syncthreads();  // wsum is reused by the next scan
+  return v + before;
+}
+
 // Histogram of digit (key >> shift) & (2^bits - 1) over keys matching the
 // current prefix.  Each wave counts into its own LDS copy (hot bins are
 // shared by many keys; separate copies keep the waves from contending), and
@@ -147,7 +166,8 @@ template <typename IO>
 __global__ void __launch_bounds__(kHistThreads) k_radix_pick(SelectState* st, const uint32_t* hist, int shift,
                                                             int bits, int last, float mult, float user_lambda,
                                                             float* d_lambda_out) {
-  __shared__ uint64_t part[kHistThreads];
+  static_assert(kHistThreads == kPickThreads, "pick_scan's block size");
+  __shared__ uint64_t wsum[kPickThreads / 64];
   __shared__ uint32_t tot[kHistBins];  // per-bin totals over the copies
   // Read before the barriers below: one thread rewrites the state at the end.
   const uint64_t want = st->rank;
@@ -162,16 +182,9 @@ __global__ void __launch_bounds__(kHistThreads) k_radix_pick(SelectState* st, co
     tot[i] = c;
     s += c;
   }
-  part[threadIdx.x] = s;
-  __syncthreads();
-  // Inclusive prefix sums of the per-thread totals (log-step scan).
-  for (int off = 1; off < kHistThreads; off <<= 1) {
-    const uint64_t v = (int)threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  const uint64_t incl = part[threadIdx.x], excl = incl - s;
+  // Inclusive prefix sums of the per-thread totals (its barriers also make
+  // every thread's tot[] visible to the scanning thread below).
+  const uint64_t incl = pick_scan(s, wsum), excl = incl - s;
   // The thread whose bins hold rank `want` (the last one if the rank were
   // past the total) scans them.
   if ((excl < want && want <= incl) || (threadIdx.x == kHistThreads - 1 && want > incl)) {
@@ -293,26 +306,8 @@ __global__ void __launch_bounds__(kSelThreads) k_hist16(const IO* M, int64_t num
 
 // One block: the key holding rank st->rank; lambda = mult * its value.
 // 256 threads: thread t holds coarse group t, then key g*128 + t of the
-// chosen group g; both prefix sums are wave scans plus the totals of the
-// waves before.
-constexpr int kPickThreads = 256;
+// chosen group g; both prefix sums are wave scans (pick_scan).
 static_assert(kSelGroups == kPickThreads && kSelGroup <= kPickThreads, "one thread per group and per key");
-
-// Inclusive prefix sum of v over the block's kPickThreads threads.
-__device__ __forceinline__ uint64_t pick_scan(uint64_t v, uint64_t* wsum) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t u = __shfl_up((unsigned long long)v, off, 64);
-    if (lane >= off) v += u;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  uint64_t before = 0;
-  for (int i = 0; i < w; ++i) before += wsum[i];
-  __syncthreads();  // wsum is reused by the next scan
-  return v + before;
-}
 
 template <typename IO>
 __global__ void __launch_bounds__(kPickThreads) k_pick16(SelectState* st, const uint32_t* hist, float mult,
